@@ -1,0 +1,303 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each pin is a function of a per-head attention implementation, so the same
+pins run against the oracle itself and against deliberately broken copies of
+it (planted on the CPU, below): every plausible slip must fail at least one
+pin.
+"""
+import inspect
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute, online
+from oracle import reference as ref
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
+TOL = 1e-12
+
+
+def attn(impl, q, k, v, scale, causal=False):
+    B, H, Nq, _ = q.shape
+    O = np.zeros((B, H, Nq, v.shape[-1]))
+    L = np.zeros((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            O[b, h], L[b, h] = impl(q[b, h], k[b, h], v[b, h], scale, causal)
+    return O, L
+
+
+def rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def close(a, b, tol=TOL):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape
+    both_inf = np.isneginf(a) & np.isneginf(b)
+    diff = np.abs(np.where(both_inf, 0.0, a) - np.where(both_inf, 0.0, b))
+    assert np.all(np.isfinite(diff)), "non-finite mismatch"
+    assert diff.max(initial=0.0) <= tol, f"max diff {diff.max()}"
+
+
+# ----------------------------------------------------------------- pins
+def pin_worked_example(impl):
+    """The scalar example of the explainer (§2) as d = 1 attention, scale 1."""
+    g = json.load(open(GOLDEN))
+    K = np.array(g["scores"], dtype=np.float64)[:, None]
+    V = np.array(g["values"], dtype=np.float64)[:, None]
+    O, L = impl(np.ones((1, 1)), K, V, 1.0, False)
+    close(O[0, 0], float(g["O"]))
+    close(L[0], float(g["LSE"]))
+    # closed form, independent of the fixture
+    e = math.exp
+    closed = (2 * e(-2) - e(-3) + 4 + 3 * e(-4)) / (e(-2) + e(-3) + 1 + e(-4))
+    close(O[0, 0], closed)
+
+
+def pin_brute(impl):
+    """Pure-Python brute force on tiny shapes, causal on and off, Nq != Nk."""
+    for (B, H, Nq, Nk, d, dv, causal, seed) in [
+        (2, 2, 5, 5, 4, 3, False, 1), (1, 2, 3, 7, 8, 8, True, 2),
+        (2, 1, 7, 3, 2, 5, True, 3), (1, 1, 9, 9, 8, 4, True, 4),
+        (1, 1, 4, 6, 3, 3, False, 5),
+    ]:
+        q, k, v = rand((B, H, Nq, d), seed), rand((B, H, Nk, d), seed + 10), rand((B, H, Nk, dv), seed + 20)
+        scale = 1 / math.sqrt(d) if d != 4 else 0.7  # includes scales float32 cannot hold exactly
+        Ob, Lb = brute.attention(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+        O, L = attn(impl, q, k, v, scale, causal)
+        close(O, Ob)
+        close(L, Lb)
+
+
+def pin_constant_k(impl):
+    """Every key equal -> equal scores -> uniform weights over the visible keys:
+    O_i = mean of visible V rows, LSE_i = s + ln n_i with n_i = number visible."""
+    for Nq, Nk, causal in [(6, 6, False), (6, 6, True), (4, 9, True), (9, 4, True), (5, 8, False)]:
+        d = 5
+        q = rand((1, 1, Nq, d), 11)
+        krow = rand((d,), 12)
+        k = np.broadcast_to(krow, (1, 1, Nk, d)).copy()
+        v = rand((1, 1, Nk, 3), 13)
+        scale = 0.3
+        O, L = attn(impl, q, k, v, scale, causal)
+        sc = float(np.float32(scale))
+        for i in range(Nq):
+            n = min(Nk, i + 1 + Nk - Nq) if causal else Nk
+            if n <= 0:
+                close(O[0, 0, i], np.zeros(3))
+                assert L[0, 0, i] == -math.inf
+                continue
+            close(O[0, 0, i], v[0, 0, :n].mean(axis=0))
+            close(L[0, 0, i], sc * float(q[0, 0, i] @ krow) + math.log(n))
+
+
+def pin_scale_zero(impl):
+    q, k, v = rand((1, 2, 5, 4), 21), rand((1, 2, 7, 4), 22), rand((1, 2, 7, 2), 23)
+    O, L = attn(impl, q, k, v, 0.0, False)
+    close(O, np.broadcast_to(v.mean(axis=2, keepdims=True), O.shape))
+    close(L, np.full(L.shape, math.log(7)))
+
+
+def pin_single_key(impl):
+    """Nk = 1: the lone key gets all the weight; LSE is its score."""
+    q, k, v = rand((1, 1, 4, 6), 31), rand((1, 1, 1, 6), 32), rand((1, 1, 1, 6), 33)
+    O, L = attn(impl, q, k, v, 0.25, False)
+    close(O[0, 0], np.broadcast_to(v[0, 0, 0], (4, 6)))
+    close(L[0, 0], 0.25 * (q[0, 0] @ k[0, 0, 0]))
+
+
+def pin_ones_v(impl):
+    """Rows of P sum to 1, so V = 1 gives O = 1 on every non-empty row."""
+    q, k = rand((1, 1, 6, 4), 41) * 5, rand((1, 1, 6, 4), 42) * 5
+    v = np.ones((1, 1, 6, 3))
+    O, _ = attn(impl, q, k, v, 0.5, True)
+    close(O, np.ones_like(O))
+
+
+def pin_shift(impl):
+    """Adding c_i to every score of row i (via an extra q/k coordinate) leaves O
+    unchanged and raises LSE_i by c_i."""
+    Nq, Nk, d = 5, 8, 4
+    q, k, v = rand((1, 1, Nq, d), 51), rand((1, 1, Nk, d), 52), rand((1, 1, Nk, 3), 53)
+    scale = 0.5
+    c = rand((Nq,), 54) * 40
+    q2 = np.concatenate([q, (c / scale)[None, None, :, None]], axis=-1)
+    k2 = np.concatenate([k, np.ones((1, 1, Nk, 1))], axis=-1)
+    O1, L1 = attn(impl, q, k, v, scale, True)
+    O2, L2 = attn(impl, q2, k2, v, scale, True)
+    close(O2, O1, 1e-11)
+    close(L2, L1 + c, 1e-11)
+
+
+def pin_online(impl):
+    """The streaming (m, l, u) recurrence of the pages reaches the same result."""
+    for Nq, Nk, causal in [(7, 7, True), (5, 11, True), (11, 5, True), (6, 9, False)]:
+        q, k, v = rand((2, 2, Nq, 8), 61) * 3, rand((2, 2, Nk, 8), 62) * 3, rand((2, 2, Nk, 4), 63)
+        O, L = attn(impl, q, k, v, 0.4, causal)
+        Oo, Lo = online.online_attention(q, k, v, 0.4, causal)
+        close(O, Oo)
+        close(L, Lo)
+
+
+def pin_sdpa(impl):
+    """torch's scaled_dot_product_attention in float64 on the CPU (tiny shapes).
+    Its is_causal is top-left aligned, so Nq != Nk uses an explicit mask."""
+    for Nq, Nk, causal in [(6, 6, False), (6, 6, True), (4, 7, True), (5, 9, False)]:
+        q, k, v = rand((2, 3, Nq, 8), 71), rand((2, 3, Nk, 8), 72), rand((2, 3, Nk, 8), 73)
+        scale = 1 / math.sqrt(8)
+        mask = None
+        if causal:
+            i = torch.arange(Nq)[:, None]
+            j = torch.arange(Nk)[None, :]
+            mask = j <= i + (Nk - Nq)
+        ref_o = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+            attn_mask=mask, scale=float(np.float32(scale))).numpy()
+        O, _ = attn(impl, q, k, v, scale, causal)
+        close(O, ref_o, 1e-12)
+
+
+PINS = [pin_worked_example, pin_brute, pin_constant_k, pin_scale_zero, pin_single_key,
+        pin_ones_v, pin_shift, pin_online, pin_sdpa]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    pin(ref.head_attention)
+
+
+# ------------------------------------------------- online / merge pins
+def test_online_worked_example():
+    g = json.load(open(GOLDEN))
+    st = online.online_row(g["scores"], g["values"])
+    o, lse = online.finish(st)
+    close(o, float(g["O"]))
+    close(lse, float(g["LSE"]))
+    # a naive exp without the max shift overflows, which is why the shift exists
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.exp(np.float64(1000.0)))
+
+
+def test_merge_worked_example():
+    g = json.load(open(GOLDEN))
+    s, v = g["scores"], g["values"]
+    left = online.summarize(s[:2], v[:2])
+    right = online.summarize(s[2:], v[2:])
+    close(left, [float(x) for x in g["left_state"]])
+    close(right, [float(x) for x in g["right_state"]])
+    merged = online.merge(left, right)
+    close(merged, [float(x) for x in g["merged_state"]])
+    close(merged[2] / merged[1], float(g["merged_O"]))
+
+
+def test_merge_invariance_every_split():
+    """Splitting a row's keys anywhere (and in many pieces) and merging the
+    block states reproduces the oracle row."""
+    rng = np.random.default_rng(5)
+    for trial in range(6):
+        n, dv = int(rng.integers(2, 40)), int(rng.integers(1, 9))
+        s = rng.standard_normal(n) * (1 + 300 * (trial % 2))
+        v = rng.standard_normal((n, dv))
+        O, L = ref.head_attention(np.ones((1, 1)), s[:, None], v, 1.0)
+        for cut in range(1, n):
+            st = online.merge(online.summarize(s[:cut], v[:cut]), online.summarize(s[cut:], v[cut:]))
+            o, lse = online.finish(st)
+            close(o, O[0], 1e-12 * max(1, np.abs(O).max()))
+            close(lse, L[0], 1e-12 * max(1.0, abs(L[0])))
+        for _ in range(5):
+            k = int(rng.integers(2, min(n, 8) + 1))
+            cuts = np.sort(rng.choice(np.arange(1, n), size=k - 1, replace=False))
+            parts = np.split(np.arange(n), cuts)
+            states = [online.summarize(s[p], v[p]) for p in parts]
+            order = rng.permutation(len(states))  # merge order must not matter
+            st = states[order[0]]
+            for j in order[1:]:
+                st = online.merge(st, states[j])
+            o, lse = online.finish(st)
+            close(o, O[0], 1e-12 * max(1, np.abs(O).max()))
+            close(lse, L[0], 1e-12 * max(1.0, abs(L[0])))
+
+
+# ---------------------------------------------------- conventions
+def test_empty_rows_causal_more_queries_than_keys():
+    q, k, v = rand((1, 1, 7, 4), 81), rand((1, 1, 3, 4), 82), rand((1, 1, 3, 4), 83)
+    O, L = oracle.attention(q, k, v, 0.5, True)
+    # bottom-right alignment: query i sees keys j <= i - 4, so rows 0..3 see none
+    assert np.all(O[0, 0, :4] == 0) and np.all(np.isneginf(L[0, 0, :4]))
+    assert np.all(np.isfinite(L[0, 0, 4:]))
+
+
+def test_attention_rows_matches_full():
+    q, k, v = rand((2, 3, 33, 8), 91), rand((2, 3, 40, 8), 92), rand((2, 3, 40, 8), 93)
+    O, L = oracle.attention(q, k, v, 0.35, True)
+    rows = [(1, 2, 0), (0, 0, 32), (1, 1, 17), (0, 2, 5), (1, 2, 31)]
+    Or, Lr = oracle.attention_rows(q, k, v, 0.35, True, rows)
+    for r, (b, h, i) in enumerate(rows):
+        close(Or[r], O[b, h, i], 1e-13)
+        close(Lr[r], L[b, h, i], 1e-13)
+
+
+def test_decode_oracle_is_fwd_at_one_query():
+    lens = torch.tensor([5, 1, 17, 9], dtype=torch.int32)
+    q, kc, vc, sl, off = workloads.decode_inputs(4, 3, 8, lens, seed=3, dtype="f32")
+    O, L = oracle.decode(q, kc, vc, sl, off, 0.3)
+    for b in range(4):
+        lo, n = int(off[b]), int(sl[b])
+        qb = q[b][:, None, :].numpy()[None]                        # [1,H,1,d]
+        kb = kc[lo:lo + n].permute(1, 0, 2).numpy()[None]           # [1,H,n,d]
+        vb = vc[lo:lo + n].permute(1, 0, 2).numpy()[None]
+        Of, Lf = oracle.attention(qb, kb, vb, 0.3, causal=True)     # Nq = 1 sees all keys
+        close(O[b], Of[0, :, 0], 1e-13)
+        close(L[b], Lf[0, :, 0], 1e-13)
+
+
+def test_accepts_bf16_tensors_exactly():
+    q, k, v = workloads.prefill_inputs(1, 2, 9, 9, 8, "bf16", seed=4)
+    O1, L1 = oracle.attention(q, k, v, 0.2, True)
+    O2, L2 = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), 0.2, True)
+    close(O1, O2, 0.0)
+    close(L1, L2, 0.0)
+
+
+# ------------------------------------------- planted mistakes (CPU only)
+MUTATIONS = {
+    "dropped_scale": ("S = f32_scale(scale) * (Q @ K.T)", "S = (Q @ K.T)"),
+    "top_left_causal": ("last_visible = q_pos + (Nk - nq_total)", "last_visible = q_pos"),
+    "causal_off_by_one": ("hidden = np.arange(Nk)[None, :] > last_visible", "hidden = np.arange(Nk)[None, :] >= last_visible"),
+    "no_max_shift": ("E = np.exp(S - m_shift[:, None])", "E = np.exp(S)"),
+    "unnormalised_P": ("P = E / np.where(empty, 1.0, l)[:, None]", "P = E"),
+    "lse_without_max": ("m_shift + np.log(", "0.0 + np.log("),
+    "reversed_values": ("O = P @ V", "O = P @ V[::-1]"),
+    "transposed_scores": ("(Q @ K.T)  #", "(K @ Q.T).T[:, ::-1]  #"),
+    "max_over_wrong_axis": ("m = S.max(axis=1)", "m = S.max(axis=1) * 0 + S.max()"),
+}
+
+
+def _mutant(name):
+    src = inspect.getsource(ref.head_attention)
+    old, new = MUTATIONS[name]
+    assert old in src, f"mutation anchor for {name} not found"
+    ns = dict(ref.__dict__)
+    exec(src.replace(old, new), ns)
+    return ns["head_attention"]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name):
+    impl = _mutant(name)
+    failed = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(impl)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"mutation {name} slipped past every pin"

@@ -1,0 +1,150 @@
+"""Seeded synthetic inputs for the exact-attention forward path.
+
+This module only draws random tensors and lays them out; it holds none of the
+attention arithmetic.  Both the HIP path (through its tests and the benchmark)
+and the CPU oracle take their inputs from here, so neither has to trust the
+other's data.
+
+Shapes follow the scenarios the pages name:
+  * GPT-2-medium attention: batch 64, 16 heads, N = 1024
+    (AI圣经13 FlashAttention review, chengyansuo.com, §02);
+  * long prefill 8192/8192, single-request decode 1/8192 and batched decode
+    with mixed history lengths (FlashAttention explainer, cztcode.com/2026/5368,
+    §6 table);
+  * head dimension 64 to 128 (AI圣经13 review, §03).
+
+Recipe: a torch.Generator on the device the tensors are made on, seeded per
+workload, draws N(0, 1) in float32; bf16 workloads round those draws to bf16
+(round-to-nearest-even).  Draw order: lengths (batched decode only), then q,
+then k, then v.  The host copy of the rounded tensors is what the oracle reads.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class PrefillSpec:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str  # "bf16" | "f32"
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs: two Nq x Nk x d contractions (QK^T and PV).
+
+        Causal work is counted as half of the dense work (the 4*B*H*N^2*d/2
+        convention)."""
+        f = 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
+        return f / 2 if self.causal else f
+
+
+@dataclass(frozen=True)
+class DecodeSpec:
+    name: str
+    B: int
+    H: int
+    d: int
+    min_len: int
+    max_len: int
+    seed: int
+    fixed_len: int | None = None  # single-request decode uses one fixed length
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# Tiny fp32 non-causal case the oracle finishes instantly.
+TINY_F32 = PrefillSpec("tiny_f32_n128_d64", 1, 1, 128, 128, 64, "f32", False, 1701)
+# GPT-2-medium-shaped attention, non-causal and causal.
+GPT2M = PrefillSpec("gpt2m_b64_h16_n1024_d64", 64, 16, 1024, 1024, 64, "bf16", False, 1702)
+GPT2M_CAUSAL = PrefillSpec("gpt2m_b64_h16_n1024_d64_causal", 64, 16, 1024, 1024, 64, "bf16", True, 1702)
+# Single-request decode over an 8192-token history.
+DECODE_SINGLE = DecodeSpec("decode_single_h32_n8192_d128", 1, 32, 128, 8192, 8192, 1703, fixed_len=8192)
+# Batched decode, 64 sequences with history lengths uniform in [128, 16384].
+DECODE_BATCHED = DecodeSpec("decode_batched_b64_h32_len128-16384_d128", 64, 32, 128, 128, 16384, 1704)
+# Long causal prefill 8192/8192.
+LONG_PREFILL = PrefillSpec("prefill_causal_h32_n8192_d128", 1, 32, 8192, 8192, 128, "bf16", True, 1705)
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _normal(shape, g, device, dtype):
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x.to(dtype) if dtype != torch.float32 else x
+
+
+def prefill_inputs(B, H, Nq, Nk, d, dtype="bf16", seed=0, device="cpu"):
+    """q [B,H,Nq,d], k [B,H,Nk,d], v [B,H,Nk,d], contiguous, N(0,1)."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = _gen(device, seed)
+    q = _normal((B, H, Nq, d), g, device, tdt)
+    k = _normal((B, H, Nk, d), g, device, tdt)
+    v = _normal((B, H, Nk, d), g, device, tdt)
+    return q, k, v
+
+
+def prefill_spec_inputs(spec: PrefillSpec, device="cpu"):
+    return prefill_inputs(spec.B, spec.H, spec.Nq, spec.Nk, spec.d, spec.dtype, spec.seed, device)
+
+
+def decode_lengths(B, min_len, max_len, seed, fixed_len=None):
+    """Per-sequence history lengths (int32, host), drawn first from the seed."""
+    if fixed_len is not None:
+        return torch.full((B,), fixed_len, dtype=torch.int32)
+    g = _gen("cpu", seed)
+    return torch.randint(min_len, max_len + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
+def decode_inputs(B, H, d, seqlens, seed=0, device="cpu", dtype="bf16"):
+    """Packed token-major cache for decode.
+
+    Returns q [B,H,d], kcache [T,H,d], vcache [T,H,d] with T = sum(seqlens),
+    seqlens int32 [B] and offsets int32 [B] (exclusive prefix sums), all on
+    `device`.  Sequence b owns cache rows offsets[b] .. offsets[b]+seqlens[b]-1.
+    """
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    seqlens = torch.as_tensor(seqlens, dtype=torch.int32).cpu()
+    offs = torch.zeros(B, dtype=torch.int64)
+    if B > 1:
+        offs[1:] = torch.cumsum(seqlens.to(torch.int64), 0)[:-1]
+    T = int(seqlens.to(torch.int64).sum())
+    g = _gen(device, seed + 7919)  # lengths use the plain seed on the host
+    q = _normal((B, H, d), g, device, tdt)
+    k = _normal((max(T, 1), H, d), g, device, tdt)[:T]
+    v = _normal((max(T, 1), H, d), g, device, tdt)[:T]
+    return (q, k.contiguous(), v.contiguous(), seqlens.to(device),
+            offs.to(torch.int32).to(device))
+
+
+def decode_spec_inputs(spec: DecodeSpec, device="cpu"):
+    lens = decode_lengths(spec.B, spec.min_len, spec.max_len, spec.seed, spec.fixed_len)
+    return decode_inputs(spec.B, spec.H, spec.d, lens, spec.seed, device)
+
+
+def decode_kv_bytes(seqlens, H, d, elem_bytes=2) -> int:
+    """Bytes of K plus V history the decode step must read."""
+    T = int(torch.as_tensor(seqlens).to(torch.int64).sum())
+    return 2 * T * H * d * elem_bytes
+
+
+def to_f64(t: torch.Tensor):
+    """Exact upcast of a (possibly bf16, possibly device) tensor to a float64 numpy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
