@@ -1,0 +1,137 @@
+/*
+ * fa.h — C ABI of an MI355X (gfx950) exact-attention forward library.
+ *
+ * What is computed.  For each (batch b, head h), with per-head matrices
+ * Q [Nq x d], K [Nk x d], V [Nk x d]:
+ *
+ *     S = scale * Q K^T,   P = softmax(S) row-wise,   O = P V,
+ *     LSE_i = ln sum_j exp(S_ij)
+ *
+ * exactly (not an approximation), but without ever writing S or P to device
+ * memory: keys are streamed tile by tile and each query row carries a running
+ * state (m = largest score so far, l = sum of exp(s - m), u = sum of
+ * exp(s - m) v), rescaled whenever m grows, with O = u / l formed once at the
+ * end.  Sources: FlashAttention explainer (cztcode.com/2026/5368) §1 for the
+ * definition and the N x N intermediates, §2 for the (m, l, u) recurrence,
+ * §3 for merging the states of two key blocks and for the saved normalisation
+ * statistics, §6 for causal block skipping and the prefill/decode split;
+ * Flash Attention wiki note (astro-wiki) "Online Softmax", "Tiling" and the
+ * FlashAttention-2 notes (query-tile-outer loop order, division deferred to
+ * the end); AI圣经13 FlashAttention review (chengyansuo.com) §03 (one fused
+ * kernel; statistics kept for recomputation; head dimension 64 to 128).
+ *
+ * Conventions (where the pages are silent):
+ *   - causal masking is bottom-right aligned: query i sees key j iff
+ *     j <= i + (Nk - Nq);
+ *   - a query row that sees no key gets O = 0 and LSE = -inf;
+ *   - LSE is float32, natural log, of the scaled scores;
+ *   - O has the dtype of the inputs.
+ *
+ * Ownership and threading.  The caller allocates and owns every buffer
+ * (inputs, outputs, workspace) and picks the stream.  The library allocates
+ * no device memory, keeps no pointer after a call returns and holds no
+ * mutable global state; calls are thread-safe.
+ *
+ * Alignment.  q, k, v, o, kcache, vcache and the workspace must be 16-byte
+ * aligned; lse, seqlens, offsets and the decode output 4-byte aligned
+ * (FA_ERR_INVALID_ARG / FA_ERR_WORKSPACE otherwise).
+ *
+ * Errors.  Every entry point returns an fa_status and never throws.  All
+ * argument checks run before any HIP call, so an invalid call has no side
+ * effect.  FA_OK means the work was enqueued on `stream` (results are valid
+ * once the stream has reached that point).  A failed launch returns
+ * FA_ERR_HIP.  Device-side contract violations (seqlens[b] > max_seqlen,
+ * cache ranges out of bounds, overlapping input/output buffers) are undefined
+ * behaviour.  There is no fallback path: an unsupported request fails.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, non-finite scale, size too large */
+  FA_ERR_UNSUPPORTED = -2, /* head dimension other than 64 or 128 */
+  FA_ERR_WORKSPACE = -3,   /* decode workspace missing or smaller than required */
+  FA_ERR_HIP = -4          /* the HIP runtime refused the launch */
+} fa_status;
+
+/*
+ * Prefill / general forward pass, bf16 inputs and output.
+ *
+ *   q   bf16 [B, H, Nq, d]  contiguous, row-major (device)
+ *   k   bf16 [B, H, Nk, d]  contiguous (device)
+ *   v   bf16 [B, H, Nk, d]  contiguous (device)
+ *   o   bf16 [B, H, Nq, d]  contiguous, written (device)
+ *   lse fp32 [B, H, Nq]     written (device)
+ *   d in {64, 128}; B, H, Nq, Nk >= 1; scale finite (usually 1/sqrt(d));
+ *   causal != 0 applies the bottom-right causal mask and skips key tiles that
+ *   lie wholly above the diagonal (explainer §6).
+ *
+ * Products of bf16 inputs accumulate in fp32; the softmax runs in fp32; P is
+ * rounded to bf16 (nearest-even) before the P V product.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+           hipStream_t stream);
+
+/*
+ * Same contract with fp32 q, k, v, o.  Arithmetic is plain fp32 throughout
+ * (no reduced-precision products).
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int Nq, int Nk, int d, float scale, int causal,
+               hipStream_t stream);
+
+/*
+ * Decode: one new query per sequence over a packed, variable-length KV cache
+ * (explainer §6: a single query sees its whole history; batched decode mixes
+ * history lengths).  Each sequence's keys are cut into chunks of `split_keys`
+ * keys that are processed in parallel; each chunk leaves a partial state
+ * (m, l, u) in the workspace and a second kernel merges the partial states of
+ * a sequence with the block-merge rule of explainer §3/§7.
+ *
+ *   q        bf16 [B, H, d]        (device)
+ *   kcache   bf16 [T, H, d]        token-major (device)
+ *   vcache   bf16 [T, H, d]        token-major (device)
+ *   seqlens  int32 [B]             history length of each sequence (device)
+ *   offsets  int32 [B]             first cache row of each sequence (device);
+ *                                  sequence b owns rows offsets[b] ..
+ *                                  offsets[b] + seqlens[b] - 1
+ *   o        bf16 [B, H, d]        written (device)
+ *   lse      fp32 [B, H]           written (device)
+ *   max_seqlen  an upper bound of seqlens[] (host; sizes the grid, so no
+ *               device-to-host copy is needed); 0 <= seqlens[b] <= max_seqlen
+ *   split_keys  keys per chunk, a positive multiple of 64, or 0 to let the
+ *               library choose (fa_decode_split_keys)
+ *   workspace   device scratch of at least fa_decode_workspace_bytes(...) bytes,
+ *               owned by the caller; its contents need no initialisation
+ *
+ * A sequence with seqlens[b] == 0 gets O = 0 and LSE = -inf.  Cache row
+ * addresses are computed in 64-bit, so T * H * d may exceed 2^31.
+ */
+int fa_decode_split_keys(int B, int H, int d, int max_seqlen);
+size_t fa_decode_workspace_bytes(int B, int H, int d, int max_seqlen, int split_keys);
+int fa_decode_varlen(const void* q, const void* kcache, const void* vcache,
+                     const int32_t* seqlens, const int32_t* offsets,
+                     void* o, float* lse,
+                     int B, int H, int d, int max_seqlen, float scale, int split_keys,
+                     void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,111 @@
+// api.cpp — the C ABI declared in include/fa.h: argument checks (all before
+// any HIP call), kernel selection and launch-status mapping.
+#include "fa.h"
+
+#include <climits>
+#include <cstdint>
+#include <cmath>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr long long kMaxGridX = 0x7fffffffLL;  // HIP grid.x limit
+constexpr long long kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool dims_ok(int B, int H, int Nq, int Nk) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return false;
+  if ((long long)B * H > INT_MAX) return false;
+  return true;
+}
+
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Nq, int Nk, int d, float scale, int causal, hipStream_t stream, bool f32) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (!dims_ok(B, H, Nq, Nk)) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const long long grid = f32 ? fa::fwd_f32_grid(B, H, Nq) : fa::fwd_bf16_grid(B, H, Nq);
+  if (grid > kMaxGridX) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal ? 1 : 0, stream};
+  const hipError_t e = f32 ? fa::launch_fwd_f32(a) : fa::launch_fwd_bf16(a);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// Chunk size for split-KV decode: start at 256 keys (one workgroup then
+// streams 128 KiB of K+V at d=128) and double while the grid would exceed
+// 32768 workgroups, so a single long sequence still spreads over every CU
+// while a large batch gets fewer, longer chunks.
+int choose_split_keys(int B, int H, int max_seqlen) {
+  long long sk = 256;
+  while (sk < max_seqlen && (long long)B * H * ((max_seqlen + sk - 1) / sk) > 32768) sk *= 2;
+  return (int)sk;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+           int Nk, int d, float scale, int causal, hipStream_t stream) {
+  return fwd_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, stream, false);
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+               int Nq, int Nk, int d, float scale, int causal, hipStream_t stream) {
+  return fwd_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, stream, true);
+}
+
+int fa_decode_split_keys(int B, int H, int d, int max_seqlen) {
+  (void)d;
+  if (B < 1 || H < 1 || max_seqlen < 1) return 0;
+  return choose_split_keys(B, H, max_seqlen);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int d, int max_seqlen, int split_keys) {
+  if (B < 1 || H < 1 || max_seqlen < 1 || (d != 64 && d != 128) || split_keys < 0) return 0;
+  const long long sk = split_keys > 0 ? split_keys : choose_split_keys(B, H, max_seqlen);
+  const long long n_splits = (max_seqlen + sk - 1) / sk;
+  return (size_t)B * (size_t)H * (size_t)n_splits * (size_t)(d + 2) * sizeof(float);
+}
+
+int fa_decode_varlen(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens,
+                     const int32_t* offsets, void* o, float* lse, int B, int H, int d,
+                     int max_seqlen, float scale, int split_keys, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !kcache || !vcache || !seqlens || !offsets || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned4(o) ||
+      !aligned4(lse) || !aligned4(seqlens) || !aligned4(offsets))
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || max_seqlen < 1) return FA_ERR_INVALID_ARG;
+  if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (split_keys < 0 || split_keys % 64 != 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const int sk = split_keys > 0 ? split_keys : choose_split_keys(B, H, max_seqlen);
+  const long long n_splits = ((long long)max_seqlen + sk - 1) / sk;
+  if (n_splits > kMaxGridX) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, max_seqlen, sk);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  fa::DecodeArgs a{q, kcache, vcache, seqlens, offsets, o, lse, B, H, d, max_seqlen, scale,
+                   sk, (int)n_splits, static_cast<float*>(workspace), stream};
+  return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime refused the launch";
+    default: return "unknown fa_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// kernels.hpp — host-side launch interface between the C ABI (api.cpp) and the
+// HIP kernels.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Nq, Nk, d;
+  float scale;
+  int causal;
+  hipStream_t stream;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* kcache;
+  const void* vcache;
+  const int32_t* seqlens;
+  const int32_t* offsets;
+  void* o;
+  float* lse;
+  int B, H, d, max_seqlen;
+  float scale;
+  int split_keys;  // resolved (> 0)
+  int n_splits;    // ceil(max_seqlen / split_keys)
+  float* ws;       // workspace, decode_workspace_floats(...) floats
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+
+// Workgroup counts, so the host can reject grids the hardware cannot launch.
+long long fwd_bf16_grid(int B, int H, int Nq);
+long long fwd_f32_grid(int B, int H, int Nq);
+
+}  // namespace fa

@@ -1,0 +1,131 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects every invalid call before touching the HIP runtime."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import io_aware_exact_17_amd as fa
+from conftest import ROOT, gpu_available
+
+HEADER = os.path.join(ROOT, "include", "fa.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+
+# Fake, suitably aligned device addresses: never dereferenced, because every
+# call below is rejected by the host-side checks (or, without a GPU, by the
+# runtime) before anything runs.
+A = 0x10000
+A2 = 0x20000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exists_and_loads():
+    assert os.path.exists(fa.LIB_PATH), "run io_aware_exact_17_amd/build.py first"
+    fa.load()
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(fa.SIGNATURES), "binding and header disagree"
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_[a-z0-9_]+)$", out, flags=re.M))
+    missing = set(names) - exported
+    assert not missing, f"not exported: {missing}"
+    lib = fa.load()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings():
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR):
+        assert fa.fa_status_string(s).startswith("FA_")
+    assert "unknown" in fa.fa_status_string(12345)
+
+
+def fwd_call(entry="fa_fwd", q=A, k=A, v=A, o=A2, lse=A2, B=1, H=1, Nq=8, Nk=8, d=64,
+             scale=0.125, causal=0):
+    lib = fa.load()
+    return getattr(lib, entry)(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f32"])
+def test_fwd_rejects_invalid_arguments(entry):
+    assert fwd_call(entry, q=None) == INVALID
+    assert fwd_call(entry, k=None) == INVALID
+    assert fwd_call(entry, v=None) == INVALID
+    assert fwd_call(entry, o=None) == INVALID
+    assert fwd_call(entry, lse=None) == INVALID
+    assert fwd_call(entry, q=A + 8) == INVALID      # not 16-byte aligned
+    assert fwd_call(entry, lse=A2 + 2) == INVALID
+    for bad in ({"B": 0}, {"H": 0}, {"Nq": 0}, {"Nk": 0}, {"B": -3}, {"Nq": -1}):
+        assert fwd_call(entry, **bad) == INVALID
+    assert fwd_call(entry, B=1 << 16, H=1 << 16) == INVALID  # B*H overflows int
+    assert fwd_call(entry, scale=float("nan")) == INVALID
+    assert fwd_call(entry, scale=float("inf")) == INVALID
+    for d in (0, 32, 63, 96, 256):
+        assert fwd_call(entry, d=d) == UNSUPPORTED
+    # grid of more than 2^31 - 1 workgroups
+    assert fwd_call(entry, B=65535, H=65535 // 2, Nq=1 << 20) == INVALID
+
+
+def dec_call(q=A, kc=A, vc=A, sl=A2, off=A2, o=A2, lse=A2, B=2, H=4, d=128, max_seqlen=100,
+             scale=0.1, split_keys=0, ws=A, ws_bytes=1 << 30):
+    lib = fa.load()
+    return lib.fa_decode_varlen(q, kc, vc, sl, off, o, lse, B, H, d, max_seqlen, scale,
+                                split_keys, ws, ws_bytes, None)
+
+
+def test_decode_rejects_invalid_arguments():
+    for kw in ("q", "kc", "vc", "sl", "off", "o", "lse"):
+        assert dec_call(**{kw: None}) == INVALID
+    assert dec_call(kc=A + 4) == INVALID
+    assert dec_call(sl=A2 + 1) == INVALID
+    for bad in ({"B": 0}, {"H": 0}, {"max_seqlen": 0}, {"B": 70000}, {"H": 70000}):
+        assert dec_call(**bad) == INVALID
+    assert dec_call(scale=float("nan")) == INVALID
+    assert dec_call(split_keys=-64) == INVALID
+    assert dec_call(split_keys=100) == INVALID  # not a multiple of 64
+    assert dec_call(d=96) == UNSUPPORTED
+    assert dec_call(ws=None) == WORKSPACE
+    assert dec_call(ws=A + 8) == WORKSPACE
+    need = fa.fa_decode_workspace_bytes(2, 4, 128, 100, 0)
+    assert dec_call(ws_bytes=need - 1) == WORKSPACE
+
+
+def test_workspace_and_split_plan():
+    # a single long sequence is cut into 256-key chunks
+    assert fa.fa_decode_split_keys(1, 32, 128, 8192) == 256
+    assert fa.fa_decode_workspace_bytes(1, 32, 128, 8192, 0) == 1 * 32 * 32 * 130 * 4
+    # a large batch gets longer chunks, keeping the grid <= 32768 workgroups
+    sk = fa.fa_decode_split_keys(64, 32, 128, 16384)
+    assert sk % 64 == 0 and 64 * 32 * -(-16384 // sk) <= 32768
+    assert fa.fa_decode_workspace_bytes(3, 5, 64, 1000, 128) == 3 * 5 * 8 * 66 * 4
+    assert fa.fa_decode_workspace_bytes(0, 5, 64, 1000, 128) == 0
+    assert fa.fa_decode_workspace_bytes(3, 5, 96, 1000, 128) == 0
+
+
+@pytest.mark.skipif(gpu_available(), reason="uses fake device pointers; only safe with no GPU")
+def test_valid_call_without_gpu_reports_hip_error():
+    # All checks pass, so the launch reaches the HIP runtime, which has no
+    # device here: the status must be FA_ERR_HIP, not a crash.
+    assert fwd_call() == HIPERR
+    assert fwd_call("fa_fwd_f32", d=128, causal=1) == HIPERR
+    assert dec_call() == HIPERR
+
+
+def test_binding_validates_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q)  # host tensors are refused
+    with pytest.raises(TypeError):
+        fa.fa_fwd(None, q, q)

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle.
+
+Tolerances: max |O - O_oracle| <= 1e-5 for fp32 inputs and <= 2e-2 for bf16
+inputs (fp32 accumulation); max |LSE - LSE_oracle| <= 1e-3 (-inf == -inf
+counts as exact).  Inputs are the seeded workloads; the oracle reads host
+copies of exactly the tensors the kernels read.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32, TOL_BF16, TOL_LSE = 1e-5, 2e-2, 1e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def max_err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    both = np.isneginf(a) & np.isneginf(b)
+    d = np.abs(np.where(both, 0.0, a) - np.where(both, 0.0, b))
+    return float(np.nan_to_num(d, nan=np.inf).max(initial=0.0))
+
+
+def check(o, lse, O, L, tol, what):
+    eo = max_err(W.to_f64(o), O)
+    el = max_err(W.to_f64(lse), L)
+    log(f"  {what}: err_O={eo:.3e} err_LSE={el:.3e}")
+    assert eo <= tol, f"{what}: err_O {eo}"
+    assert el <= TOL_LSE, f"{what}: err_LSE {el}"
+    return eo, el
+
+
+def run_fwd(fa, q, k, v, scale, causal):
+    f = fa.fa_fwd_f32 if q.dtype == torch.float32 else fa.fa_fwd
+    o, lse = f(q, k, v, scale, causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ------------------------------------------------------------- configs
+def test_tiny_f32(fa):
+    s = W.TINY_F32
+    log(f"case {s.name}")
+    q, k, v = W.prefill_spec_inputs(s, "cuda")
+    o, lse = run_fwd(fa, q, k, v, s.scale, s.causal)
+    O, L = oracle.attention(q, k, v, s.scale, s.causal)
+    check(o, lse, O, L, TOL_F32, s.name)
+
+
+def _sampled_rows(B, H, Nq, n_heads, n_rows, seed):
+    rng = np.random.default_rng(seed)
+    rows = []
+    heads = [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(n_heads)]
+    heads += [(0, 0), (B - 1, H - 1)]
+    for b, h in heads:
+        idx = set(rng.integers(0, Nq, n_rows).tolist()) | {0, 1, 127, 128, Nq - 1}
+        rows += [(b, h, i) for i in sorted(i for i in idx if i < Nq)]
+    return rows
+
+
+@pytest.mark.parametrize("spec", [W.GPT2M, W.GPT2M_CAUSAL, W.LONG_PREFILL], ids=lambda s: s.name)
+def test_prefill_full_size_sampled(fa, spec):
+    """The benchmark shapes, in the launch configuration the benchmark times;
+    the oracle evaluates sampled rows one by one."""
+    log(f"case {spec.name}")
+    q, k, v = W.prefill_spec_inputs(spec, "cuda")
+    o, lse = run_fwd(fa, q, k, v, spec.scale, spec.causal)
+    rows = _sampled_rows(spec.B, spec.H, spec.Nq, 6, 48, spec.seed)
+    O, L = oracle.attention_rows(q, k, v, spec.scale, spec.causal, rows)
+    idx = tuple(torch.as_tensor(a, device=o.device) for a in np.array(rows).T)
+    og = o[idx].cpu()
+    lg = lse[idx].cpu()
+    check(og, lg, O, L, TOL_BF16, spec.name)
+    # every output is finite, every LSE finite (no empty rows in these shapes)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_prefill_gpt2m_whole_heads(fa):
+    """Complete heads of the GPT-2-medium shape, every row, causal and not."""
+    for spec in (W.GPT2M, W.GPT2M_CAUSAL):
+        log(f"case {spec.name} whole heads")
+        q, k, v = W.prefill_spec_inputs(spec, "cuda")
+        o, lse = run_fwd(fa, q, k, v, spec.scale, spec.causal)
+        for b, h in [(0, 0), (17, 5), (63, 15)]:
+            O, L = oracle.head_attention(q[b, h], k[b, h], v[b, h], spec.scale, spec.causal)
+            check(o[b, h], lse[b, h], O, L, TOL_BF16, f"{spec.name} b={b} h={h}")
+
+
+# ------------------------------------------------------------- edge shapes
+EDGE = [
+    # B, H, Nq, Nk, d, causal
+    (1, 2, 200, 200, 128, False), (1, 2, 200, 200, 128, True),
+    (2, 1, 200, 200, 64, False), (2, 1, 200, 200, 64, True),
+    (1, 2, 100, 300, 128, True), (1, 2, 300, 100, 128, True),
+    (1, 1, 300, 100, 64, True), (1, 3, 1, 777, 128, False), (1, 1, 1, 1, 64, False),
+    (1, 1, 129, 65, 128, False), (1, 1, 64, 64, 128, True), (1, 1, 4, 1000, 64, True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(map(str, s)))
+def test_edge_shapes(fa, shape, dtype):
+    B, H, Nq, Nk, d, causal = shape
+    log(f"case edge {shape} {dtype}")
+    q, k, v = W.prefill_inputs(B, H, Nq, Nk, d, dtype, seed=Nq * 7 + Nk + d, device="cuda")
+    scale = 1 / math.sqrt(d)
+    o, lse = run_fwd(fa, q, k, v, scale, causal)
+    O, L = oracle.attention(q, k, v, scale, causal)
+    check(o, lse, O, L, TOL_F32 if dtype == "f32" else TOL_BF16, f"{shape} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
+def test_unusual_scales(fa, dtype, scale):
+    log(f"case scale {scale} {dtype}")
+    q, k, v = W.prefill_inputs(1, 2, 150, 170, 128, dtype, seed=5, device="cuda")
+    o, lse = run_fwd(fa, q, k, v, scale, True)
+    O, L = oracle.attention(q, k, v, scale, True)
+    check(o, lse, O, L, TOL_F32 if dtype == "f32" else TOL_BF16, f"scale={scale} {dtype}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_scores(fa, d):
+    """Scores near 1000 (the explainer's §2 example magnitude): the running
+    maximum keeps exp finite."""
+    log(f"case large scores d={d}")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    B, H, N = 1, 2, 256
+    scale = 1 / math.sqrt(d)
+    e = torch.randn(d, generator=g, device="cuda")
+    e = e / e.norm() * math.sqrt(1000 / scale)          # scale * |e|^2 = 1000
+    q = (torch.randn(B, H, N, d, generator=g, device="cuda") + e).to(torch.bfloat16)
+    k = (torch.randn(B, H, N, d, generator=g, device="cuda") + e).to(torch.bfloat16)
+    v = torch.randn(B, H, N, d, generator=g, device="cuda").to(torch.bfloat16)
+    for causal in (False, True):
+        o, lse = run_fwd(fa, q, k, v, scale, causal)
+        O, L = oracle.attention(q, k, v, scale, causal)
+        assert L.min() > 900
+        check(o, lse, O, L, TOL_BF16, f"large scores d={d} causal={causal}")
+
+
+def test_deterministic(fa):
+    log("case determinism")
+    q, k, v = W.prefill_inputs(2, 4, 520, 520, 128, "bf16", seed=9, device="cuda")
+    o1, l1 = run_fwd(fa, q, k, v, 0.088, True)
+    o2, l2 = run_fwd(fa, q, k, v, 0.088, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------- decode
+def run_decode(fa, q, kc, vc, sl, off, max_len, scale, split_keys=0):
+    o, lse = fa.fa_decode_varlen(q, kc, vc, sl, off, max_len, scale, split_keys)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def test_decode_single_full(fa):
+    s = W.DECODE_SINGLE
+    log(f"case {s.name}")
+    q, kc, vc, sl, off = W.decode_spec_inputs(s, "cuda")
+    o, lse = run_decode(fa, q, kc, vc, sl, off, s.max_len, s.scale)
+    O, L = oracle.decode(q, kc, vc, sl.cpu(), off.cpu(), s.scale)
+    check(o, lse, O, L, TOL_BF16, s.name)
+
+
+def test_decode_batched_full_size_sampled(fa):
+    s = W.DECODE_BATCHED
+    log(f"case {s.name}")
+    q, kc, vc, sl, off = W.decode_spec_inputs(s, "cuda")
+    log(f"  T={kc.shape[0]} tokens, {kc.numel() * 4 / 1e9:.2f} GB of K+V")
+    o, lse = run_decode(fa, q, kc, vc, sl, off, s.max_len, s.scale)
+    slh, offh = sl.cpu(), off.cpu()
+    seqs = sorted({0, s.B - 1, int(torch.argmax(slh)), int(torch.argmin(slh)), 7, 31})
+    O, L = oracle.decode(q, kc, vc, slh, offh, s.scale, seqs=seqs)
+    check(o[seqs], lse[seqs], O[seqs], L[seqs], TOL_BF16, s.name + " sampled sequences")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_edge_lengths(fa, d):
+    lens = [1, 0, 128, 16384, 63, 65, 257, 5000]
+    log(f"case decode edge lengths d={d}")
+    q, kc, vc, sl, off = W.decode_inputs(len(lens), 4, d, lens, seed=17, device="cuda")
+    scale = 1 / math.sqrt(d)
+    for sk in (0, 64, 1024):
+        o, lse = run_decode(fa, q, kc, vc, sl, off, max(lens), scale, sk)
+        O, L = oracle.decode(q, kc, vc, sl.cpu(), off.cpu(), scale)
+        check(o, lse, O, L, TOL_BF16, f"d={d} split_keys={sk}")
+        assert (o[1] == 0).all() and torch.isneginf(lse[1]).all()
+
+
+def test_decode_split_invariance(fa):
+    s = W.DECODE_SINGLE
+    log("case decode split invariance")
+    q, kc, vc, sl, off = W.decode_spec_inputs(s, "cuda")
+    ref_o, ref_l = run_decode(fa, q, kc, vc, sl, off, s.max_len, s.scale, 8192)
+    for sk in (64, 128, 256, 512, 2048):
+        o, lse = run_decode(fa, q, kc, vc, sl, off, s.max_len, s.scale, sk)
+        el = (lse - ref_l).abs().max().item()
+        eo = (o.float() - ref_o.float()).abs().max().item()
+        log(f"  split_keys={sk}: dLSE={el:.2e} dO={eo:.2e}")
+        assert el <= 1e-5 and eo <= 2 ** -7
+
+
+def test_decode_matches_fwd_single_query(fa):
+    log("case decode vs fwd Nq=1")
+    lens = [300, 1000, 77]
+    q, kc, vc, sl, off = W.decode_inputs(3, 2, 128, lens, seed=23, device="cuda")
+    o, lse = run_decode(fa, q, kc, vc, sl, off, 1000, 0.088)
+    for b, n in enumerate(lens):
+        lo = int(off[b])
+        qb = q[b][None, :, None, :].contiguous()
+        kb = kc[lo:lo + n].permute(1, 0, 2)[None].contiguous()
+        vb = vc[lo:lo + n].permute(1, 0, 2)[None].contiguous()
+        of, lf = run_fwd(fa, qb, kb, vb, 0.088, False)
+        assert (lf[0, :, 0] - lse[b]).abs().max().item() <= 1e-4
+        assert (of[0, :, 0].float() - o[b].float()).abs().max().item() <= 2e-2
