@@ -1,0 +1,232 @@
+"""Benchmark of the exact-attention forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-budget SECONDS]
+
+One step is one pass of the whole hot path over resident synthetic inputs:
+  1. fa_fwd      causal prefill, B=1, H=32, Nq=Nk=8192, d=128, bf16
+  2. fa_decode_varlen  batched decode, 64 sequences x 32 heads, d=128, history
+                 lengths uniform in [128, 16384] (packed bf16 K/V cache)
+  3. fa_decode_varlen  single-request decode, 32 heads, 8192-token history
+The batched decode streams ~8.7 GB, far more than the 256 MB last-level
+cache, so the single-request decode that follows reads its 128 MiB of K/V
+from HBM.  Every call is bracketed by HIP events on the stream it runs on.
+
+Prints one JSON line: `value` is the prefill rate in TFLOP/s (4*B*H*N^2*d/2
+algorithmic FLOPs over the prefill kernel's event time); the decode KV-read
+rates (GB/s) ride along in `decode`; `roofline` describes the prefill kernel
+against the bf16 dense matrix-core peak; `cpu_baseline` times the fp64 oracle
+on a bounded sample of the prefill on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd TFLOP/s @ causal N=8192 d=128 bf16; decode KV-read GB/s"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBPS = 8000.0      # HBM3E
+# HBM bytes per prefill launch from rocprofv3 FETCH_SIZE + WRITE_SIZE at this
+# workload, each scaled by what the counter reads for a plain 1 GiB copy
+# (FETCH x2.0, WRITE x1.0): 335673 KiB x 2 + 66597 KiB.  Reset to None
+# whenever the prefill kernel changes until the counters are taken again.
+PREFILL_TRAFFIC_BYTES = 755653632
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cpu-budget", type=float, default=12.0,
+                   help="seconds of host time for the oracle baseline sample")
+    return p.parse_args()
+
+
+def cpu_baseline(budget_s: float):
+    """The fp64 oracle (as it stands) on whole heads of the causal prefill
+    workload, one head at a time until the budget is spent (at least one)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max(i.get("num_threads", 1) for i in threadpool_info())
+    except Exception:
+        threads = torch.get_num_threads()
+    s = W.LONG_PREFILL
+    g = torch.Generator().manual_seed(s.seed)
+    heads = 0
+    flops = 0.0
+    t_total = 0.0
+    while heads == 0 or t_total < budget_s:
+        q = torch.randn(s.Nq, s.d, generator=g).to(torch.bfloat16).double().numpy()
+        k = torch.randn(s.Nk, s.d, generator=g).to(torch.bfloat16).double().numpy()
+        v = torch.randn(s.Nk, s.d, generator=g).to(torch.bfloat16).double().numpy()
+        t0 = time.perf_counter()
+        oracle.head_attention(q, k, v, s.scale, causal=True)
+        t_total += time.perf_counter() - t0
+        heads += 1
+        flops += 4.0 * s.Nq * s.Nk * s.d / 2
+        if heads >= s.H:
+            break
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {s.H} heads of the causal N=8192 d=128 prefill, whole heads, "
+                      f"fp64 NumPy with S and P materialised; {t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not a measured configuration.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import io_aware_exact_17_amd as fa
+    import workloads as W
+
+    fa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    P = W.LONG_PREFILL
+    DB = W.DECODE_BATCHED
+    DS = W.DECODE_SINGLE
+    q, k, v = W.prefill_spec_inputs(P, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(P.B, P.H, P.Nq, dtype=torch.float32, device=dev)
+
+    dbq, dbk, dbv, dbl, dbo = W.decode_spec_inputs(DB, dev)
+    lens_b = dbl.cpu()
+    db_out = torch.empty_like(dbq)
+    db_lse = torch.empty(DB.B, DB.H, dtype=torch.float32, device=dev)
+    db_sk = fa.fa_decode_split_keys(DB.B, DB.H, DB.d, DB.max_len)
+    db_ws = torch.empty(fa.fa_decode_workspace_bytes(DB.B, DB.H, DB.d, DB.max_len, 0),
+                        dtype=torch.uint8, device=dev)
+
+    dsq, dsk, dsv, dsl, dso = W.decode_spec_inputs(DS, dev)
+    ds_out = torch.empty_like(dsq)
+    ds_lse = torch.empty(DS.B, DS.H, dtype=torch.float32, device=dev)
+    ds_sk = fa.fa_decode_split_keys(DS.B, DS.H, DS.d, DS.max_len)
+    ds_ws = torch.empty(fa.fa_decode_workspace_bytes(DS.B, DS.H, DS.d, DS.max_len, 0),
+                        dtype=torch.uint8, device=dev)
+
+    # A plain copy of known size, untimed: its HBM counters calibrate the
+    # prefill kernel's FETCH_SIZE / WRITE_SIZE when this script runs under
+    # rocprofv3 --pmc.
+    cal_src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    del cal_src, cal_dst
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(rec):
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        e0.record(stream)
+        fa.fa_fwd(q, k, v, P.scale, True, out=o, lse=lse)
+        e1.record(stream)
+        fa.fa_decode_varlen(dbq, dbk, dbv, dbl, dbo, DB.max_len, DB.scale, 0, out=db_out,
+                            lse=db_lse, workspace=db_ws)
+        e2.record(stream)
+        fa.fa_decode_varlen(dsq, dsk, dsv, dsl, dso, DS.max_len, DS.scale, 0, out=ds_out,
+                            lse=ds_lse, workspace=ds_ws)
+        e3.record(stream)
+        if rec is not None:
+            rec.append((e0, e1, e2, e3))
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+
+    recs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_pre = [a.elapsed_time(b) for a, b, _, _ in recs]
+    t_db = [b.elapsed_time(c) for _, b, c, _ in recs]
+    t_ds = [c.elapsed_time(d) for _, _, c, d in recs]
+    ms_step = wall * 1e3 / args.steps
+
+    flops = P.flops()
+    pre_ms = statistics.mean(t_pre)
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    db_bytes = W.decode_kv_bytes(lens_b, DB.H, DB.d)
+    ds_bytes = W.decode_kv_bytes(dsl.cpu(), DS.H, DS.d)
+    db_gbps = db_bytes / (statistics.mean(t_db) * 1e-3) / 1e9
+    ds_gbps = ds_bytes / (statistics.mean(t_ds) * 1e-3) / 1e9
+
+    cpu = cpu_baseline(args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal prefill B=1 H=32 N=8192 d=128 + batched varlen decode "
+                        "64 seqs x 32 heads d=128 len U[128,16384] + single decode H=32 N=8192 d=128",
+            "prefill": {"B": P.B, "H": P.H, "Nq": P.Nq, "Nk": P.Nk, "d": P.d, "causal": True,
+                        "seed": P.seed, "flops": flops, "ms_mean": round(pre_ms, 4),
+                        "ms_median": round(statistics.median(t_pre), 4),
+                        "ms_min": round(min(t_pre), 4)},
+            "decode_batched": {"B": DB.B, "H": DB.H, "d": DB.d, "seed": DB.seed,
+                               "tokens": int(lens_b.sum()), "kv_bytes": db_bytes,
+                               "split_keys": db_sk, "ms_mean": round(statistics.mean(t_db), 4)},
+            "decode_single": {"B": DS.B, "H": DS.H, "Nk": DS.fixed_len, "d": DS.d,
+                              "kv_bytes": ds_bytes, "split_keys": ds_sk,
+                              "ms_mean": round(statistics.mean(t_ds), 4)},
+        },
+        "decode": {"unit": "GB/s",
+                   "batched_kv_read": round(db_gbps, 1),
+                   "single_kv_read": round(ds_gbps, 1),
+                   "frac_of_hbm_peak": {"batched": round(db_gbps / PEAK_HBM_GBPS, 4),
+                                        "single": round(ds_gbps / PEAK_HBM_GBPS, 4)}},
+        "roofline": {
+            "kernel": "fwd_bf16_kernel<128, causal>",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": PREFILL_TRAFFIC_BYTES,
+        },
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count, "torch": torch.__version__,
+                   "hip": torch.version.hip},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -83,13 +83,13 @@ int fa_decode_varlen(const void* q, const void* kcache, const void* vcache, cons
       !aligned4(lse) || !aligned4(seqlens) || !aligned4(offsets))
     return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || max_seqlen < 1) return FA_ERR_INVALID_ARG;
-  if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_INVALID_ARG;
+  if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_INVALID_ARG;  // grid.z / grid.x
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (split_keys < 0 || split_keys % 64 != 0) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   const int sk = split_keys > 0 ? split_keys : choose_split_keys(B, H, max_seqlen);
   const long long n_splits = ((long long)max_seqlen + sk - 1) / sk;
-  if (n_splits > kMaxGridX) return FA_ERR_INVALID_ARG;
+  if (n_splits > kMaxGridYZ) return FA_ERR_INVALID_ARG;  // chunks index grid.y
   const size_t need = fa_decode_workspace_bytes(B, H, d, max_seqlen, sk);
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
   fa::DecodeArgs a{q, kcache, vcache, seqlens, offsets, o, lse, B, H, d, max_seqlen, scale,

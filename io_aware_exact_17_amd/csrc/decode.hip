@@ -9,7 +9,7 @@
 // workgroups to cover every CU even for one sequence.
 //
 // Each sequence's keys are cut into chunks of `split_keys`.  A workgroup of
-// the split kernel streams one (sequence, head, chunk): every key row (d
+// the split kernel streams one (head, chunk, sequence): every key row (d
 // bf16 = 256 B at d=128) is read by a group of d/8 lanes, 16 bytes each; the
 // q.k dot product is finished with DPP row reductions; each lane group keeps
 // the running state (m, l, u) of the explainer's §2 recurrence, updated once
@@ -47,7 +47,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     float* __restrict__ ws_u, float* __restrict__ ws_ml, int H, int split_keys, int n_splits,
     float c) {
   using C = DecCfg<D>;
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Heads vary fastest across the grid, so the workgroups running together
+  // read neighbouring 256-byte head slices of the same token rows.
+  const int h = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
   const int len = seqlens[b];
   const int k_begin = s * split_keys;
   if (k_begin >= len) return;  // chunk past this sequence's end
@@ -151,7 +153,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
   }
 }
 
-// One wave per (sequence, head); each lane finishes two output dims.
+// One wave per (sequence, head).  The chunk states are read in parallel: each
+// lane holds one chunk's (m, l) for the wave-wide maximum and weight, then
+// every lane accumulates two output dims over the chunks, taking the chunk
+// weights from the lane that computed them.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     const float* __restrict__ ws_u, const float* __restrict__ ws_ml,
@@ -162,22 +178,35 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   const int len = seqlens[b];
   const int n = min(n_splits, len > 0 ? (len + split_keys - 1) / split_keys : 0);
   const size_t slot0 = ((size_t)b * H + h) * n_splits;
+
   float M = kNegInf;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, ws_ml[(slot0 + s) * 2]);
-  float L = 0.f, U0 = 0.f, U1 = 0.f;
+  for (int s = lane; s < n; s += 64) M = fmaxf(M, ws_ml[(slot0 + s) * 2]);
+  M = wave_max(M);
+  float Lp = 0.f;
+  for (int s = lane; s < n; s += 64)
+    Lp = __builtin_fmaf(exp2_hw(ws_ml[(slot0 + s) * 2] - M), ws_ml[(slot0 + s) * 2 + 1], Lp);
+  const float L = wave_sum(Lp);
+
   const int d0 = 2 * lane;
-  for (int s = 0; s < n; ++s) {
-    const float f = exp2_hw(ws_ml[(slot0 + s) * 2] - M);
-    L = __builtin_fmaf(f, ws_ml[(slot0 + s) * 2 + 1], L);
-    if (d0 < D) {
-      const f32x2 w = *reinterpret_cast<const f32x2*>(ws_u + (slot0 + s) * D + d0);
-      U0 = __builtin_fmaf(f, w[0], U0);
-      U1 = __builtin_fmaf(f, w[1], U1);
+  const bool has_d = d0 < D;
+  float U0 = 0.f, U1 = 0.f;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int s_l = c0 + lane;
+    const float f_l = s_l < n ? exp2_hw(ws_ml[(slot0 + s_l) * 2] - M) : 0.f;
+    const int cnt = min(64, n - c0);
+#pragma unroll 8
+    for (int j = 0; j < cnt; ++j) {
+      const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f_l), j));
+      if (has_d) {
+        const f32x2 w = *reinterpret_cast<const f32x2*>(ws_u + (slot0 + c0 + j) * D + d0);
+        U0 = __builtin_fmaf(f, w[0], U0);
+        U1 = __builtin_fmaf(f, w[1], U1);
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   const size_t orow = ((size_t)b * H + h) * D;
-  if (d0 < D) *reinterpret_cast<uint32_t*>(O + orow + d0) = pack_bf16x2(U0 * inv, U1 * inv);
+  if (has_d) *reinterpret_cast<uint32_t*>(O + orow + d0) = pack_bf16x2(U0 * inv, U1 * inv);
   if (lane == 0) LSE[(size_t)b * H + h] = L > 0.f ? (M + log2_hw(L)) * kLn2 : kNegInf;
 }
 
@@ -191,7 +220,7 @@ hipError_t launch(const DecodeArgs& a) {
                     (void*)&a.offsets, (void*)&ws_u, (void*)&ws_ml, (void*)&a.H,
                     (void*)&a.split_keys, (void*)&a.n_splits, (void*)&c};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<D>),
-                                   dim3((unsigned)a.n_splits, (unsigned)a.H, (unsigned)a.B),
+                                   dim3((unsigned)a.H, (unsigned)a.n_splits, (unsigned)a.B),
                                    dim3(kThreads), args, 0, a.stream);
     if (e != hipSuccess) return e;
   }

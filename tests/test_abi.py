@@ -93,6 +93,7 @@ def test_decode_rejects_invalid_arguments():
     assert dec_call(scale=float("nan")) == INVALID
     assert dec_call(split_keys=-64) == INVALID
     assert dec_call(split_keys=100) == INVALID  # not a multiple of 64
+    assert dec_call(split_keys=64, max_seqlen=64 * 65536, ws_bytes=1 << 40) == INVALID  # > 65535 chunks
     assert dec_call(d=96) == UNSUPPORTED
     assert dec_call(ws=None) == WORKSPACE
     assert dec_call(ws=A + 8) == WORKSPACE
