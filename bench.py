@@ -36,7 +36,7 @@ PEAK_HBM_GBPS = 8000.0      # HBM3E
 # workload, each scaled by what the counter reads for a plain 1 GiB copy
 # (FETCH x2.0, WRITE x1.0): 335673 KiB x 2 + 66597 KiB.  Reset to None
 # whenever the prefill kernel changes until the counters are taken again.
-PREFILL_TRAFFIC_BYTES = 755653632
+PREFILL_TRAFFIC_BYTES = None
 
 
 def parse():

@@ -103,14 +103,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int qi = wq0 + col;        // this lane's query row
 
   // Q^T operand: lane holds Q[qi][16s + 8*half + 0..7] for every k-step s.
+  // Rows past Nq read row Nq-1 (their results are never stored).
   bf16x8 qf[C::KS];
   {
-    const bool ok = qi < Nq;
-    const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)(ok ? qi : 0) * D);
+    const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)min(qi, Nq - 1) * D);
     const uint32_t flip = negate_q ? 0x80008000u : 0u;  // exact sign flip for a negative scale
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      u32x4 w = ok ? src[2 * s + half] : u32x4{0, 0, 0, 0};
+      u32x4 w = src[2 * s + half];
       w ^= flip;
       qf[s] = __builtin_bit_cast(bf16x8, w);
     }
@@ -122,21 +122,41 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int vkg = tid % C::KGROUPS;  // 4-key group of the V block this thread moves
   const int vdb = tid / C::KGROUPS;  // 8-wide d block
 
+  // Per-lane byte offsets inside a tile (the tile base is uniform, so loads
+  // take an SGPR base plus a 32-bit lane offset).  Keys past Nk read row
+  // Nk-1 instead: finite values whose scores are masked to -inf, so they
+  // carry zero weight.  Only a ragged last tile clamps.
+  uint32_t koff[C::KCHUNKS], voff[4];
+#pragma unroll
+  for (int i = 0; i < C::KCHUNKS; ++i) {
+    const int ch = tid + kThreads * i;
+    koff[i] = (uint32_t)(((ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) voff[r] = (uint32_t)(((4 * vkg + r) * D + vdb * 8) * 2);
+
   auto load_tile = [&](int j) {
     const int k0 = j * BC;
+    const char* Kt = reinterpret_cast<const char*>(K + kbase + (size_t)k0 * D);
+    const char* Vt = reinterpret_cast<const char*>(V + kbase + (size_t)k0 * D);
+    if (k0 + BC <= Nk) {
 #pragma unroll
-    for (int i = 0; i < C::KCHUNKS; ++i) {
-      const int ch = tid + kThreads * i;
-      const int key = ch / (D / 8), cc = ch % (D / 8);
-      const int gk = k0 + key;
-      kreg[i] = gk < Nk ? *reinterpret_cast<const u32x4*>(K + kbase + (size_t)gk * D + cc * 8)
-                        : u32x4{0, 0, 0, 0};
-    }
+      for (int i = 0; i < C::KCHUNKS; ++i) kreg[i] = *reinterpret_cast<const u32x4*>(Kt + koff[i]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int gk = k0 + 4 * vkg + r;
-      vreg[r] = gk < Nk ? *reinterpret_cast<const u32x4*>(V + kbase + (size_t)gk * D + vdb * 8)
-                        : u32x4{0, 0, 0, 0};
+      for (int r = 0; r < 4; ++r) vreg[r] = *reinterpret_cast<const u32x4*>(Vt + voff[r]);
+    } else {
+      const int last = Nk - 1 - k0;
+#pragma unroll
+      for (int i = 0; i < C::KCHUNKS; ++i) {
+        const int ch = tid + kThreads * i;
+        const uint32_t o = (uint32_t)((min(ch / (D / 8), last) * D + (ch % (D / 8)) * 8) * 2);
+        kreg[i] = *reinterpret_cast<const u32x4*>(Kt + o);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t o = (uint32_t)((min(4 * vkg + r, last) * D + vdb * 8) * 2);
+        vreg[r] = *reinterpret_cast<const u32x4*>(Vt + o);
+      }
     }
   };
 
@@ -185,16 +205,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       const bf16* sv = sk + C::KTILE;
 
       // S^T = K Q^T for this tile: NKB blocks of 32 keys x 32 queries.
+      // The NKB accumulators are independent; alternating them keeps
+      // consecutive matrix instructions free of dependences.
       f32x16 sacc[C::NKB];
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-        sacc[kb] = f32x16{};
+      for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
+      for (int s = 0; s < C::KS; ++s)
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + (kb * 32 + col) * C::KROW + s * 16 + half * 8);
           sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
         }
-      }
 
       // Mask keys past the end and, on diagonal tiles, keys after the query.
       const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wq0 + off);
@@ -216,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
       mx = max_across_halves(mx);
-      const float mt = (mx == kNegInf) ? kNegInf : mx * c;
+      const float mt = mx * c;  // c > 0, so -inf stays -inf
 
       // Move the reference only when the tile max exceeds it by > 2^tau.
       const bool grow = mt > m_ref + kLazyTau;
@@ -237,12 +259,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          float p0 = exp2_hw(__builtin_fmaf(sacc[kb][r], c, -m_use));
-          float p1 = exp2_hw(__builtin_fmaf(sacc[kb][r + 1], c, -m_use));
-          if (need_mask) {  // -inf * 0 would be NaN when the scale is zero
-            p0 = sacc[kb][r] == kNegInf ? 0.f : p0;
-            p1 = sacc[kb][r + 1] == kNegInf ? 0.f : p1;
-          }
+          const float p0 = exp2_hw(__builtin_fmaf(sacc[kb][r], c, -m_use));
+          const float p1 = exp2_hw(__builtin_fmaf(sacc[kb][r + 1], c, -m_use));
           lsum += p0 + p1;
           pk[kb][r >> 1] = pack_bf16x2(p0, p1);
         }
@@ -289,7 +307,10 @@ template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a) {
   const int n_qtiles = (a.Nq + kBR - 1) / kBR;
   const int BH = a.B * a.H;
-  const float c = fabsf(a.scale) * kLog2e;
+  // c > 0 keeps masked scores (-inf) at -inf after scaling.  A zero scale
+  // becomes 1e-30: every product with a finite score then rounds away
+  // against the reference, so the weights are exactly uniform, as for 0.
+  const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   const int neg = a.scale < 0.f ? 1 : 0;
   const dim3 grid((unsigned)(n_qtiles * BH));
   const dim3 block(kThreads);
