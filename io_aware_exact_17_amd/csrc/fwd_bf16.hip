@@ -12,26 +12,35 @@
 // causal diagonal are never loaded (explainer §6).
 //
 // Mapping to CDNA4:
-//  * 4 waves x 32 query rows = 128 rows per workgroup.  Both products run on
-//    the matrix cores as v_mfma_f32_32x32x16_bf16.
-//  * The score tile is formed transposed, S^T = K Q^T, so every lane holds one
-//    query column: the row max and row sum are in-lane reductions plus one
+//  * 8 waves x 32 query rows = 256 rows per workgroup, one workgroup per CU,
+//    two waves per SIMD.  Both products run on the matrix cores as
+//    v_mfma_f32_32x32x16_bf16.
+//  * The score tile is formed transposed, S^T = K Q^T, so every lane holds
+//    one query column: row max and row sum are in-lane reductions plus one
 //    exchange between lane halves (v_permlane32_swap); no reduction crosses
-//    waves.  The accumulator registers of S^T, rounded to bf16, are directly
-//    the B operand of O^T += V^T P^T, so P never leaves registers.
-//  * K tiles are staged row-major in LDS; V tiles are staged transposed
-//    (V^T, keys contiguous) with the key order permuted inside each group of
-//    16 so that one 16-byte LDS read yields exactly the 8 keys a lane's P
-//    registers hold.  Row strides are padded by 16 bytes so that the 16-byte
-//    LDS reads of 32 different rows are free of bank conflicts.
-//  * LDS is double-buffered: the next tile is fetched from HBM into registers
-//    with 16-byte loads while the current one is used, then written to the
-//    other buffer; one barrier per tile.
-//  * exp is evaluated as 2^x on v_exp_f32 with log2(e) folded into the scale.
-//    The reference maximum is only moved when a tile's maximum exceeds it by
-//    more than 2^8 (probabilities stay <= 256 before rounding to bf16), which
-//    skips most rescales of the output accumulator without changing the
-//    mathematics.
+//    waves.  The S^T accumulators, rounded to bf16, are directly the B operand
+//    of O^T += V^T P^T, so P never leaves registers.
+//  * Two wave groups in opposite phase.  Waves 0-3 (group A) handle each key
+//    tile as  S = K Q^T -> softmax -> O += P V;  waves 4-7 (group B, one on
+//    each SIMD next to a group-A wave) as  O += P V of the previous tile ->
+//    S = K Q^T -> softmax.  After each barrier the two waves sharing a SIMD
+//    therefore run their vector-ALU softmax while the other one feeds the
+//    matrix core, instead of both waiting on the same unit.
+//  * K tiles are staged row-major in LDS; V tiles transposed (V^T, keys
+//    contiguous) with the key order permuted inside each group of 16 so that
+//    one 16-byte LDS read yields exactly the 8 keys a lane's P registers hold.
+//    Row strides are padded by 16 bytes (no bank conflicts).  Two K buffers
+//    and three V^T buffers (group B reads the previous V tile); one barrier
+//    per tile.  The tile after the next is fetched from HBM into registers
+//    with 16-byte loads a whole tile ahead: waves 0-3 move V tiles
+//    (transposing them in registers), waves 4-7 move K tiles.
+//  * exp is 2^x on v_exp_f32 with log2(e) folded into the scale.  The
+//    reference maximum is not recomputed per tile: P is formed against the
+//    current reference and only when a tile's P sum exceeds 2^8 (so some P
+//    could exceed 256 before rounding to bf16) is the exact row maximum
+//    taken, the reference moved and the output accumulator rescaled.  That
+//    happens on the first tile and rarely afterwards; the mathematics is
+//    unchanged because the final division uses the same reference.
 //  * Workgroups are issued heaviest query tile first; consecutive workgroup
 //    ids walk the heads, so when B*H is a multiple of 8 every tile of a head
 //    lands on the same XCD (workgroups are dealt round-robin to the 8 XCDs)
@@ -43,29 +52,33 @@ namespace fa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBR = 128;          // query rows per workgroup
-constexpr float kLazyTau = 8.0f;  // log2 headroom before the reference max moves
+constexpr int kThreads = 512;
+constexpr int kMovers = 256;      // threads staging each operand
+constexpr int kBR = 256;          // query rows per workgroup (8 waves x 32)
+constexpr int kKBuf = 2;          // LDS K buffers
+constexpr int kVBuf = 3;          // LDS V^T buffers
+constexpr float kSumBound = 256.f;  // a tile's P sum per lane half stays <= 2^8
+constexpr int kPrefetch = 6;      // LDS operand reads kept ahead of the matrix cores
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BC = 8192 / D;   // keys per tile: 64 for d=128, 128 for d=64
-  static constexpr int KS = D / 16;     // k-steps of S^T = K Q^T
-  static constexpr int NKB = BC / 32;   // 32-key blocks per tile
-  static constexpr int NDB = D / 32;    // 32-row blocks of O^T
-  static constexpr int KROW = D + 8;    // LDS row stride of K (elements)
-  static constexpr int VROW = BC + 8;   // LDS row stride of V^T (elements)
+  static constexpr int BC = 8192 / D;    // keys per tile: 64 for d=128, 128 for d=64
+  static constexpr int KS = D / 16;      // k-steps of S^T = K Q^T
+  static constexpr int NKB = BC / 32;    // 32-key blocks per tile
+  static constexpr int NDB = D / 32;     // 32-row blocks of O^T
+  static constexpr int KROW = D + 8;     // LDS row stride of K (elements)
+  static constexpr int VROW = BC + 8;    // LDS row stride of V^T (elements)
   static constexpr int KTILE = BC * KROW;
   static constexpr int VTILE = D * VROW;
-  static constexpr int STAGE = KTILE + VTILE;
-  static constexpr int KCHUNKS = BC * D / 8 / kThreads;  // 16-byte K chunks per thread
-  static constexpr int KGROUPS = BC / 4;                 // 4-key groups of a V tile
-  static_assert(KCHUNKS * kThreads * 8 == BC * D, "K tile must split evenly");
-  static_assert(KGROUPS * (D / 8) == kThreads, "one 4x8 V block per thread");
+  static constexpr int KCHUNKS = BC * D / 8 / kMovers;   // 16-byte K chunks per K mover
+  static constexpr int VBLOCKS = (BC / 4) * (D / 8);     // 4-key x 8-dim V blocks per tile
+  static constexpr int LDS_ELEMS = kKBuf * KTILE + kVBuf * VTILE;
+  static_assert(KCHUNKS == 4 && KCHUNKS * kMovers * 8 == BC * D, "K tile split");
+  static_assert(VBLOCKS == kMovers, "one V block per V mover");
 };
 
-// Position of key `k` (0..15) inside its group of 16 in the V^T layout:
-// the two middle groups of four are swapped, so positions 8h..8h+7 hold keys
+// Position of a group of four keys inside its group of 16 in the V^T layout:
+// the two middle groups are swapped, so positions 8h..8h+7 hold keys
 // {4h..4h+3, 8+4h..8+4h+3} — the keys accumulator registers 0..7 of lane
 // half h cover in the S^T layout.
 __device__ __forceinline__ int vt_pos4(int group4) {
@@ -79,11 +92,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     float c, int negate_q, int n_qtiles) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 smem[C::LDS_ELEMS];
+  bf16* const sK = smem;                      // kKBuf K tiles
+  bf16* const sV = smem + kKBuf * C::KTILE;   // kVBuf V^T tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const bool group_b = wave >= 4;
   const int col = lane & 31;   // query column of this lane in S^T / O^T
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group this lane holds
 
@@ -95,19 +111,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const size_t qbase = (size_t)bh * Nq * D;
   const size_t kbase = (size_t)bh * Nk * D;
 
-  int kv_end = Nk;
-  if (CAUSAL) kv_end = min(Nk, q0 + kBR + off);
+  const int kv_end = CAUSAL ? min(Nk, q0 + kBR + off) : Nk;
   const int n_tiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
 
   const int wq0 = q0 + wave * 32;  // first query row of this wave
   const int qi = wq0 + col;        // this lane's query row
+  const int kv_end_w = CAUSAL ? min(Nk, wq0 + 32 + off) : Nk;
+  const int nt_w = kv_end_w > 0 ? (kv_end_w + BC - 1) / BC : 0;  // tiles this wave needs
 
-  // Q^T operand: lane holds Q[qi][16s + 8*half + 0..7] for every k-step s.
-  // Rows past Nq read row Nq-1 (their results are never stored).
+  // Q^T operand: lane holds Q[qi][16s + 8*half + 0..7].  Rows past Nq read
+  // row Nq-1 (their results are never stored).
   bf16x8 qf[C::KS];
   {
-    const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)min(qi, Nq - 1) * D);
     const uint32_t flip = negate_q ? 0x80008000u : 0u;  // exact sign flip for a negative scale
+    const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)min(qi, Nq - 1) * D);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       u32x4 w = src[2 * s + half];
@@ -116,172 +133,198 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
   }
 
-  // Staging registers for the next tile.
-  u32x4 kreg[C::KCHUNKS];
-  u32x4 vreg[4];
-  const int vkg = tid % C::KGROUPS;  // 4-key group of the V block this thread moves
-  const int vdb = tid / C::KGROUPS;  // 8-wide d block
+  // ---------------------------------------------------------- tile staging
+  // Waves 0-3 move V, waves 4-7 move K, four 16-byte chunks per thread.
+  //   K mover mt: chunks mt + 256 i of the row-major tile, i.e. key
+  //     mt / (D/8) + (256 / (D/8)) i, 8 dims at (mt % (D/8)) * 8.
+  //   V mover mt: keys 4*vkg .. 4*vkg+3 of dims vdb*8 .. vdb*8+7, written to
+  //     V^T transposed.
+  const bool k_mover = tid >= kMovers;
+  const int mt = tid & (kMovers - 1);
+  constexpr int kKeysPerPass = kMovers / (D / 8);
+  const int vkg = mt % (BC / 4);
+  const int vdb = mt / (BC / 4);
+  const int first_key = k_mover ? mt / (D / 8) : 4 * vkg;
+  const int key_step = k_mover ? kKeysPerPass : 1;
+  const int dcol = k_mover ? (mt % (D / 8)) * 8 : vdb * 8;
+  u32x4 stg[4];
 
-  // Per-lane byte offsets inside a tile (the tile base is uniform, so loads
-  // take an SGPR base plus a 32-bit lane offset).  Keys past Nk read row
-  // Nk-1 instead: finite values whose scores are masked to -inf, so they
-  // carry zero weight.  Only a ragged last tile clamps.
-  uint32_t koff[C::KCHUNKS], voff[4];
-#pragma unroll
-  for (int i = 0; i < C::KCHUNKS; ++i) {
-    const int ch = tid + kThreads * i;
-    koff[i] = (uint32_t)(((ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) voff[r] = (uint32_t)(((4 * vkg + r) * D + vdb * 8) * 2);
-
+  // The tile base is uniform, so loads take an SGPR base plus a 32-bit lane
+  // byte offset.  Keys past Nk read row Nk-1 instead: finite values whose
+  // scores are masked to -inf, so they carry zero weight.
   auto load_tile = [&](int j) {
     const int k0 = j * BC;
-    const char* Kt = reinterpret_cast<const char*>(K + kbase + (size_t)k0 * D);
-    const char* Vt = reinterpret_cast<const char*>(V + kbase + (size_t)k0 * D);
-    if (k0 + BC <= Nk) {
-#pragma unroll
-      for (int i = 0; i < C::KCHUNKS; ++i) kreg[i] = *reinterpret_cast<const u32x4*>(Kt + koff[i]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vreg[r] = *reinterpret_cast<const u32x4*>(Vt + voff[r]);
-    } else {
-      const int last = Nk - 1 - k0;
-#pragma unroll
-      for (int i = 0; i < C::KCHUNKS; ++i) {
-        const int ch = tid + kThreads * i;
-        const uint32_t o = (uint32_t)((min(ch / (D / 8), last) * D + (ch % (D / 8)) * 8) * 2);
-        kreg[i] = *reinterpret_cast<const u32x4*>(Kt + o);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t o = (uint32_t)((min(4 * vkg + r, last) * D + vdb * 8) * 2);
-        vreg[r] = *reinterpret_cast<const u32x4*>(Vt + o);
-      }
-    }
-  };
-
-  auto store_tile = [&](int stage) {
-    bf16* sk = smem + stage * C::STAGE;
-    bf16* sv = sk + C::KTILE;
-#pragma unroll
-    for (int i = 0; i < C::KCHUNKS; ++i) {
-      const int ch = tid + kThreads * i;
-      const int key = ch / (D / 8), cc = ch % (D / 8);
-      *reinterpret_cast<u32x4*>(sk + key * C::KROW + cc * 8) = kreg[i];
-    }
-    // 4 keys x 8 dims -> 8 rows of V^T, 4 keys each.
-    const int pos = 16 * (vkg >> 2) + 4 * vt_pos4(vkg & 3);
+    const char* base = reinterpret_cast<const char*>((k_mover ? K : V) + kbase + (size_t)k0 * D);
+    const int last = Nk - 1 - k0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t e01 = __builtin_amdgcn_perm(vreg[1][i], vreg[0][i], 0x05040100u);
-      const uint32_t e23 = __builtin_amdgcn_perm(vreg[3][i], vreg[2][i], 0x05040100u);
-      const uint32_t o01 = __builtin_amdgcn_perm(vreg[1][i], vreg[0][i], 0x07060302u);
-      const uint32_t o23 = __builtin_amdgcn_perm(vreg[3][i], vreg[2][i], 0x07060302u);
-      *reinterpret_cast<u32x2*>(sv + (vdb * 8 + 2 * i) * C::VROW + pos) = u32x2{e01, e23};
-      *reinterpret_cast<u32x2*>(sv + (vdb * 8 + 2 * i + 1) * C::VROW + pos) = u32x2{o01, o23};
+      const int key = min(first_key + key_step * i, last);
+      stg[i] = *reinterpret_cast<const u32x4*>(base + (uint32_t)((key * D + dcol) * 2));
+    }
+  };
+  auto store_tile = [&](int j) {
+    if (k_mover) {
+      bf16* sk = sK + (j % kKBuf) * C::KTILE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(sk + (first_key + key_step * i) * C::KROW + dcol) = stg[i];
+    } else {
+      bf16* sv = sV + (j % kVBuf) * C::VTILE;
+      // 4 keys x 8 dims -> 8 rows of V^T, 4 keys each.
+      const int pos = 16 * (vkg >> 2) + 4 * vt_pos4(vkg & 3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t e01 = __builtin_amdgcn_perm(stg[1][i], stg[0][i], 0x05040100u);
+        const uint32_t e23 = __builtin_amdgcn_perm(stg[3][i], stg[2][i], 0x05040100u);
+        const uint32_t o01 = __builtin_amdgcn_perm(stg[1][i], stg[0][i], 0x07060302u);
+        const uint32_t o23 = __builtin_amdgcn_perm(stg[3][i], stg[2][i], 0x07060302u);
+        *reinterpret_cast<u32x2*>(sv + (vdb * 8 + 2 * i) * C::VROW + pos) = u32x2{e01, e23};
+        *reinterpret_cast<u32x2*>(sv + (vdb * 8 + 2 * i + 1) * C::VROW + pos) = u32x2{o01, o23};
+      }
     }
   };
 
+  // ------------------------------------------------------ per-tile stages
   f32x16 oacc[C::NDB];
 #pragma unroll
   for (int i = 0; i < C::NDB; ++i) oacc[i] = f32x16{};
   float m_ref = kNegInf;  // reference maximum, log2 units (score * c)
   float l_part = 0.f;     // this lane half's share of the row sum
+  f32x16 sacc[C::NKB];
+  uint32_t pk[C::NKB][8];  // bf16 P pairs of the latest softmax
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  // Matrix-core loops keep kPrefetch LDS operand reads in flight: the
+  // schedule is pinned to  kPrefetch reads, then (1 MFMA, 1 read) pairs,
+  // then the remaining MFMAs, so no MFMA waits on a read issued just before.
+  auto pipeline_schedule = [&](auto n_mfma) {
+    constexpr int N = decltype(n_mfma)::value;
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kPrefetch < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int stage = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
-
-    const int k0 = j * BC;
-    const bool wave_active = !CAUSAL || k0 <= wq0 + 31 + off;
-    if (wave_active) {
-      const bf16* sk = smem + stage * C::STAGE;
-      const bf16* sv = sk + C::KTILE;
-
-      // S^T = K Q^T for this tile: NKB blocks of 32 keys x 32 queries.
-      // The NKB accumulators are independent; alternating them keeps
-      // consecutive matrix instructions free of dependences.
-      f32x16 sacc[C::NKB];
+  // The wave feeding the matrix core runs at raised issue priority, so the
+  // neighbouring wave's vector work fills the gaps instead of delaying it.
+  auto qk = [&](int j) {
+    __builtin_amdgcn_s_setprio(1);
+    const bf16* sk = sK + (j % kKBuf) * C::KTILE + col * C::KROW + half * 8;
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16{};
+    for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < C::KS; ++s)
+    for (int s = 0; s < C::KS; ++s)
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + (kb * 32 + col) * C::KROW + s * 16 + half * 8);
-          sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
-        }
-
-      // Mask keys past the end and, on diagonal tiles, keys after the query.
-      const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wq0 + off);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(Nk - 1, qi + off) : Nk - 1;
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key > lim) sacc[kb][r] = kNegInf;
-          }
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + kb * 32 * C::KROW + s * 16);
+        sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
       }
+    pipeline_schedule(std::integral_constant<int, C::KS * C::NKB>{});
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-      // Row maximum of this tile (in-lane, then across the lane halves).
+  auto pv = [&](int j) {
+    __builtin_amdgcn_s_setprio(1);
+    const bf16* sv = sV + (j % kVBuf) * C::VTILE + col * C::VROW + half * 8;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, u32x4{pk[kb][4 * t], pk[kb][4 * t + 1], pk[kb][4 * t + 2], pk[kb][4 * t + 3]});
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sv + db * 32 * C::VROW + (2 * kb + t) * 16);
+          oacc[db] = mfma_32x32x16(a, b, oacc[db]);
+        }
+      }
+    pipeline_schedule(std::integral_constant<int, C::NKB * 2 * C::NDB>{});
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Masks keys past the end and, on diagonal tiles, keys after the query;
+  // then P = 2^(s*c - m) against the current reference m, the row sum and
+  // the bf16 pairs of P.  The reference only has to keep every P small, so
+  // instead of a row maximum per tile the tile's own sum decides: if any
+  // lane's share exceeds 2^tau (or is not finite: m = -inf before the first
+  // visible key), the wave takes the exact path once — row maximum, new
+  // reference, O and l rescaled, P recomputed.  Either way every P <= 2^tau.
+  auto exp_tile = [&](float m_use, float& lsum) {
+    lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = exp2_hw(__builtin_fmaf(sacc[kb][r], c, -m_use));
+        const float p1 = exp2_hw(__builtin_fmaf(sacc[kb][r + 1], c, -m_use));
+        lsum += p0 + p1;
+        pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+      }
+  };
+  auto softmax = [&](int j) {
+    const int k0 = j * BC;
+    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wq0 + off);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(Nk - 1, qi + off) : Nk - 1;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key > lim) sacc[kb][r] = kNegInf;
+        }
+    }
+    float lsum;
+    exp_tile(m_ref, lsum);  // m_ref = -inf gives +inf/NaN sums, caught below
+    if (wave_any(!(lsum <= kSumBound))) {
       float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
       mx = max_across_halves(mx);
-      const float mt = mx * c;  // c > 0, so -inf stays -inf
-
-      // Move the reference only when the tile max exceeds it by > 2^tau.
-      const bool grow = mt > m_ref + kLazyTau;
-      if (wave_any(grow)) {
-        const float m_new = grow ? mt : m_ref;
-        const float alpha = grow ? exp2_hw(m_ref - m_new) : 1.f;  // 0 when m_ref was -inf
+      const float m_new = fmaxf(m_ref, mx * c);  // c > 0, so -inf stays -inf
+      if (m_new != m_ref) {
+        const float alpha = exp2_hw(m_ref - m_new);  // 0 when m_ref was -inf
         l_part *= alpha;
 #pragma unroll
         for (int i = 0; i < C::NDB; ++i) oacc[i] *= alpha;
         m_ref = m_new;
       }
-      const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
-
-      // P = 2^(s*c - m), its row sum, and bf16 pairs for the P^T operand.
-      uint32_t pk[C::NKB][8];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2_hw(__builtin_fmaf(sacc[kb][r], c, -m_use));
-          const float p1 = exp2_hw(__builtin_fmaf(sacc[kb][r + 1], c, -m_use));
-          lsum += p0 + p1;
-          pk[kb][r >> 1] = pack_bf16x2(p0, p1);
-        }
-      l_part += lsum;
-
-      // O^T += V^T P^T over the tile's keys, 16 keys per step.
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u32x4 pw = {pk[kb][4 * t], pk[kb][4 * t + 1], pk[kb][4 * t + 2], pk[kb][4 * t + 3]};
-          const bf16x8 b = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-          for (int db = 0; db < C::NDB; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(sv + (db * 32 + col) * C::VROW + (2 * kb + t) * 16 + half * 8);
-            oacc[db] = mfma_32x32x16(a, b, oacc[db]);
-          }
-        }
+      exp_tile(m_ref == kNegInf ? 0.f : m_ref, lsum);
     }
+    l_part += lsum;
+  };
 
-    if (j + 1 < n_tiles) store_tile(stage ^ 1);
+  // ------------------------------------------------------------- main loop
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (n_tiles > 1) load_tile(1);
+  }
+  __syncthreads();
+
+  // Group B finishes the previous tile's P V first, so it runs one extra
+  // iteration after the last tile.
+  for (int j = 0; j <= n_tiles; ++j) {
+    if (!group_b) {
+      if (j < nt_w) {
+        qk(j);
+        softmax(j);
+        pv(j);
+      }
+    } else {
+      if (j >= 1 && j - 1 < nt_w) pv(j - 1);
+      if (j < nt_w) {
+        qk(j);
+        softmax(j);
+      }
+    }
+    // Stage tile j+1 (loaded one iteration ago) and fetch tile j+2.
+    if (j + 1 < n_tiles) store_tile(j + 1);
+    if (j + 2 < n_tiles) load_tile(j + 2);
     __syncthreads();
   }
 
