@@ -97,7 +97,8 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  * history lengths).  Each sequence's keys are cut into chunks of `split_keys`
  * keys that are processed in parallel; each chunk leaves a partial state
  * (m, l, u) in the workspace and a second kernel merges the partial states of
- * a sequence with the block-merge rule of explainer §3/§7.
+ * a sequence with the block-merge rule of explainer §3/§7 (a sequence that
+ * fits in one chunk is finished by the first kernel).
  *
  *   q        bf16 [B, H, d]        (device)
  *   kcache   bf16 [T, H, d]        token-major (device)
@@ -110,10 +111,12 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  *   lse      fp32 [B, H]           written (device)
  *   max_seqlen  an upper bound of seqlens[] (host; sizes the grid, so no
  *               device-to-host copy is needed); 0 <= seqlens[b] <= max_seqlen
- *   split_keys  keys per chunk, a positive multiple of 64, or 0 to let the
- *               library choose (fa_decode_split_keys)
+ *   split_keys  keys per chunk, a positive multiple of 64 giving at most 256
+ *               chunks for max_seqlen, or 0 to let the library choose
+ *               (fa_decode_split_keys)
  *   workspace   device scratch of at least fa_decode_workspace_bytes(...) bytes,
- *               owned by the caller; its contents need no initialisation
+ *               owned by the caller; its contents need no initialisation.
+ *               Calls that run at the same time must not share a workspace.
  *
  * A sequence with seqlens[b] == 0 gets O = 0 and LSE = -inf.  Cache row
  * addresses are computed in 64-bit, so T * H * d may exceed 2^31.

@@ -149,7 +149,8 @@ def fa_decode_varlen(q, kcache, vcache, seqlens, offsets, max_seqlen, scale=None
                      out=None, lse=None, workspace=None, stream=None):
     """Decode over a packed cache: q [B,H,d], kcache/vcache [T,H,d] bf16,
     seqlens/offsets int32 [B] on the device; max_seqlen a host int >= every
-    seqlens[b].  Returns (O bf16 [B,H,d], LSE fp32 [B,H])."""
+    seqlens[b].  A caller-provided workspace is a uint8 tensor of at least
+    fa_decode_workspace_bytes bytes.  Returns (O bf16 [B,H,d], LSE fp32 [B,H])."""
     import torch
 
     lib = load()

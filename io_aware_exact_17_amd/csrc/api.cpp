@@ -12,6 +12,7 @@ namespace {
 
 constexpr long long kMaxGridX = 0x7fffffffLL;  // HIP grid.x limit
 constexpr long long kMaxGridYZ = 65535;
+constexpr long long kMaxChunks = 256;  // chunks per sequence the merge kernel combines
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -39,11 +40,14 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
 
 // Chunk size for split-KV decode: start at 256 keys (one workgroup then
 // streams 128 KiB of K+V at d=128) and double while the grid would exceed
-// 32768 workgroups, so a single long sequence still spreads over every CU
-// while a large batch gets fewer, longer chunks.
+// 32768 workgroups or a sequence would have more than 256 chunks, so a single
+// long sequence still spreads over every CU while a large batch gets fewer,
+// longer chunks.
 int choose_split_keys(int B, int H, int max_seqlen) {
   long long sk = 256;
-  while (sk < max_seqlen && (long long)B * H * ((max_seqlen + sk - 1) / sk) > 32768) sk *= 2;
+  while (sk < max_seqlen && ((long long)B * H * ((max_seqlen + sk - 1) / sk) > 32768 ||
+                             (max_seqlen + sk - 1) / sk > kMaxChunks))
+    sk *= 2;
   return (int)sk;
 }
 
@@ -71,6 +75,7 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int max_seqlen, int split_
   if (B < 1 || H < 1 || max_seqlen < 1 || (d != 64 && d != 128) || split_keys < 0) return 0;
   const long long sk = split_keys > 0 ? split_keys : choose_split_keys(B, H, max_seqlen);
   const long long n_splits = (max_seqlen + sk - 1) / sk;
+  // chunk states: u[d] per (sequence, head, chunk), then (m, l) per chunk
   return (size_t)B * (size_t)H * (size_t)n_splits * (size_t)(d + 2) * sizeof(float);
 }
 
@@ -89,7 +94,7 @@ int fa_decode_varlen(const void* q, const void* kcache, const void* vcache, cons
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   const int sk = split_keys > 0 ? split_keys : choose_split_keys(B, H, max_seqlen);
   const long long n_splits = ((long long)max_seqlen + sk - 1) / sk;
-  if (n_splits > kMaxGridYZ) return FA_ERR_INVALID_ARG;  // chunks index grid.y
+  if (n_splits > kMaxChunks) return FA_ERR_INVALID_ARG;
   const size_t need = fa_decode_workspace_bytes(B, H, d, max_seqlen, sk);
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
   fa::DecodeArgs a{q, kcache, vcache, seqlens, offsets, o, lse, B, H, d, max_seqlen, scale,

@@ -1,23 +1,24 @@
-// decode.hip — single-query attention over a packed variable-length KV cache:
-// a split-KV partial kernel and a log-sum-exp merge kernel.
+// decode.hip — single-query attention over a packed variable-length KV cache.
 //
 // With one new query per sequence the score row is 1 x history and there is
 // no N x N matrix; the cost is reading the cached keys and values (and, for a
 // single request, the launch itself): FlashAttention explainer
-// (cztcode.com/2026/5368) §6.  The kernels are therefore bandwidth kernels:
-// no matrix cores, 16-byte loads, many loads in flight per lane, and enough
-// workgroups to cover every CU even for one sequence.
+// (cztcode.com/2026/5368) §6.  These are bandwidth kernels: no matrix cores,
+// 16-byte loads, two batches of loads in flight per lane, enough workgroups
+// to cover every CU even for one sequence, and a merge built from parallel
+// loads so that it costs a few memory latencies.
 //
 // Each sequence's keys are cut into chunks of `split_keys`.  A workgroup of
-// the split kernel streams one (head, chunk, sequence): every key row (d
-// bf16 = 256 B at d=128) is read by a group of d/8 lanes, 16 bytes each; the
-// q.k dot product is finished with DPP row reductions; each lane group keeps
-// the running state (m, l, u) of the explainer's §2 recurrence, updated once
-// per batch of keys; the workgroup's lane groups are then merged through LDS
-// and one partial state per chunk goes to the workspace.  The merge kernel
-// combines a sequence's chunk states with the block-merge rule of explainer
-// §3/§7 (m = max, l and u rescaled by exp(m_i - m) and added) and writes
-// O = u / l and LSE = m + ln l.  Cache row addresses are 64-bit.
+// the split kernel streams one (head, chunk, sequence): every key row (d bf16
+// = 256 B at d=128) is read by a group of d/8 lanes, 16 bytes each; the q.k
+// dot product is finished with DPP row reductions; each lane group keeps the
+// running state (m, l, u) of the explainer's §2 recurrence, updated once per
+// batch of keys; the lane groups are merged through LDS with the block-merge
+// rule of explainer §3/§7 (m = max, l and u rescaled by exp(m_i - m) and
+// added).  A sequence that fits in one chunk is finished on the spot;
+// otherwise the chunk's state goes to the workspace and the merge kernel
+// combines a sequence's chunk states with the same rule, writing O = u / l
+// and LSE = m + ln l.  Cache row addresses are 64-bit.
 #include "cdna4.hpp"
 #include "kernels.hpp"
 
@@ -29,9 +30,9 @@ constexpr int kThreads = 256;
 
 template <int D>
 struct DecCfg {
-  static constexpr int LPR = D / 8;            // lanes per key row (16 B each)
-  static constexpr int NRG = kThreads / LPR;   // key rows covered per pass
-  static constexpr int U = D == 128 ? 16 : 8;  // keys per lane group per batch
+  static constexpr int LPR = D / 8;           // lanes per key row (16 B each)
+  static constexpr int NRG = kThreads / LPR;  // key rows covered per pass
+  static constexpr int U = 8;                 // keys per lane group per batch
 };
 
 template <int D>
@@ -40,29 +41,49 @@ __device__ __forceinline__ float row_sum(float x) {
   else return sum_row8(x);
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ seqlens, const int32_t* __restrict__ offsets,
-    float* __restrict__ ws_u, float* __restrict__ ws_ml, int H, int split_keys, int n_splits,
-    float c) {
+    bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ ws_u,
+    float* __restrict__ ws_ml, int H, int split_keys, int n_splits, float c) {
   using C = DecCfg<D>;
   // Heads vary fastest across the grid, so the workgroups running together
   // read neighbouring 256-byte head slices of the same token rows.
   const int h = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
   const int len = seqlens[b];
+  const size_t bh = (size_t)b * H + h;
+  if (len <= 0) {  // empty history: O = 0, LSE = -inf
+    if (s == 0) {
+      if (tid < D / 2) *reinterpret_cast<uint32_t*>(O + bh * D + 2 * tid) = 0u;
+      if (tid == 0) LSE[bh] = kNegInf;
+    }
+    return;
+  }
   const int k_begin = s * split_keys;
   if (k_begin >= len) return;  // chunk past this sequence's end
   const int k_end = min(len, k_begin + split_keys);
+  const int n_active = min(n_splits, (len + split_keys - 1) / split_keys);
   const size_t base = (size_t)offsets[b];
 
-  const int tid = threadIdx.x;
   const int sub = tid % C::LPR;  // which 8 dims of the row this lane reads
   const int rg = tid / C::LPR;   // lane group
 
   float qv[8];
   {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(q + ((size_t)b * H + h) * D + sub * 8);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(q + bh * D + sub * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       qv[2 * i] = bf16_lo(w[i]);
@@ -79,20 +100,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) u[e] = 0.f;
 
-  for (int k = k_begin + rg; k < k_end; k += C::NRG * C::U) {
-    u32x4 kr[C::U], vr[C::U];
+  // Batch t covers keys k_begin + rg + NRG*(U*t + i), i < U.  Two batches of
+  // loads are in flight: the next one is issued before the current one is
+  // consumed.  Keys past k_end read the chunk's first key (in range, finite)
+  // and are given score -inf.
+  constexpr int kStep = C::NRG * C::U;
+  u32x4 kA[C::U], vA[C::U], kB[C::U], vB[C::U];
+  auto load = [&](u32x4 (&kr)[C::U], u32x4 (&vr)[C::U], int k0) {
 #pragma unroll
     for (int i = 0; i < C::U; ++i) {
-      const int kk = k + C::NRG * i;
-      kr[i] = kk < k_end ? *reinterpret_cast<const u32x4*>(kp + (base + kk) * row_stride)
-                         : u32x4{0, 0, 0, 0};
+      int kk = k0 + C::NRG * i;
+      kk = kk < k_end ? kk : k_begin;
+      kr[i] = *reinterpret_cast<const u32x4*>(kp + (base + kk) * row_stride);
+      vr[i] = *reinterpret_cast<const u32x4*>(vp + (base + kk) * row_stride);
     }
-#pragma unroll
-    for (int i = 0; i < C::U; ++i) {
-      const int kk = k + C::NRG * i;
-      vr[i] = kk < k_end ? *reinterpret_cast<const u32x4*>(vp + (base + kk) * row_stride)
-                         : u32x4{0, 0, 0, 0};
-    }
+  };
+  auto consume = [&](const u32x4 (&kr)[C::U], const u32x4 (&vr)[C::U], int k0) {
     float sc[C::U];
     float mx = kNegInf;
 #pragma unroll
@@ -104,11 +127,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
         part = __builtin_fmaf(qv[2 * e + 1], bf16_hi(kr[i][e]), part);
       }
       const float dot = row_sum<D>(part);
-      sc[i] = (k + C::NRG * i < k_end) ? dot * c : kNegInf;
+      sc[i] = (k0 + C::NRG * i < k_end) ? dot * c : kNegInf;
       mx = fmaxf(mx, sc[i]);
     }
-    const float m_new = fmaxf(m, mx);  // finite: key k itself is in range
-    const float alpha = exp2_hw(m - m_new);
+    if (mx == kNegInf) return;  // no key of this batch for this lane group
+    const float m_new = fmaxf(m, mx);
+    const float alpha = exp2_hw(m - m_new);  // 0 while m = -inf
     l *= alpha;
 #pragma unroll
     for (int e = 0; e < 8; ++e) u[e] *= alpha;
@@ -123,9 +147,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
       }
     }
     m = m_new;
+  };
+
+  const int k_first = k_begin + rg;
+  if (k_first < k_end) {
+    load(kA, vA, k_first);
+    for (int k0 = k_first;; k0 += 2 * kStep) {
+      const bool more1 = k0 + kStep < k_end;
+      if (more1) load(kB, vB, k0 + kStep);
+      consume(kA, vA, k0);
+      if (!more1) break;
+      const bool more2 = k0 + 2 * kStep < k_end;
+      if (more2) load(kA, vA, k0 + 2 * kStep);
+      consume(kB, vB, k0 + kStep);
+      if (!more2) break;
+    }
   }
 
-  // Merge the lane groups' states (block-merge rule) through LDS.
+  // Merge the lane groups' states (block-merge rule) through LDS; wave 0
+  // finishes the chunk, each of its lanes owning dims 2*lane and 2*lane+1.
   __shared__ float sm_m[C::NRG], sm_l[C::NRG];
   __shared__ float sm_u[C::NRG][D + 4];
   if (sub == 0) {
@@ -135,99 +175,116 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) sm_u[rg][sub * 8 + e] = u[e];
   __syncthreads();
-  if (tid < D) {
-    float M = kNegInf;
-    for (int g = 0; g < C::NRG; ++g) M = fmaxf(M, sm_m[g]);
-    float L = 0.f, Uacc = 0.f;
-    for (int g = 0; g < C::NRG; ++g) {
-      const float f = exp2_hw(sm_m[g] - M);  // empty groups (m = -inf) weigh 0
-      L = __builtin_fmaf(f, sm_l[g], L);
-      Uacc = __builtin_fmaf(f, sm_u[g][tid], Uacc);
-    }
-    const size_t slot = ((size_t)b * H + h) * n_splits + s;
-    ws_u[slot * D + tid] = Uacc;
-    if (tid == 0) {
-      ws_ml[slot * 2] = M;
-      ws_ml[slot * 2 + 1] = L;
+  if (tid >= 64) return;
+  const int lane = tid;
+  const int d0 = 2 * lane;
+  const bool has_d = d0 < D;
+  float M = kNegInf, L = 0.f, U0 = 0.f, U1 = 0.f;
+  for (int g = 0; g < C::NRG; ++g) M = fmaxf(M, sm_m[g]);
+  for (int g = 0; g < C::NRG; ++g) {
+    const float f = exp2_hw(sm_m[g] - M);  // empty groups (m = -inf) weigh 0
+    L = __builtin_fmaf(f, sm_l[g], L);
+    if (has_d) {
+      U0 = __builtin_fmaf(f, sm_u[g][d0], U0);
+      U1 = __builtin_fmaf(f, sm_u[g][d0 + 1], U1);
     }
   }
+
+  if (n_active == 1) {  // the whole history was this chunk
+    const float inv = 1.f / L;
+    if (has_d) *reinterpret_cast<uint32_t*>(O + bh * D + d0) = pack_bf16x2(U0 * inv, U1 * inv);
+    if (lane == 0) LSE[bh] = (M + log2_hw(L)) * kLn2;
+    return;
+  }
+
+  // Leave this chunk's state for the merge kernel.
+  const size_t slot = bh * n_splits + s;
+  if (has_d) *reinterpret_cast<f32x2*>(ws_u + slot * D + d0) = f32x2{U0, U1};
+  if (lane == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{M, L};
 }
 
-// One wave per (sequence, head).  The chunk states are read in parallel: each
-// lane holds one chunk's (m, l) for the wave-wide maximum and weight, then
-// every lane accumulates two output dims over the chunks, taking the chunk
-// weights from the lane that computed them.
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
+// One 256-thread workgroup per (sequence, head) merges the chunk states.
+// Every chunk's (m, l) is requested at once, together with the sequence
+// length, and the four waves then split the chunks for the u sums, so the
+// merge costs a few memory latencies rather than one per chunk.  Sequences
+// that fitted in one chunk were finished by the split kernel.
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(
     const float* __restrict__ ws_u, const float* __restrict__ ws_ml,
     const int32_t* __restrict__ seqlens, bf16* __restrict__ O, float* __restrict__ LSE, int H,
     int split_keys, int n_splits) {
   const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t bh = (size_t)b * H + h;
+  const size_t slot0 = bh * n_splits;
+  __shared__ float sm_f[kThreads];
+  __shared__ float sm_red[2][4];
+  __shared__ float sm_part[4][D];
+
   const int len = seqlens[b];
+  // chunk states requested before the length is known (unused slots are
+  // never read as numbers: they are discarded by a select)
+  f32x2 ml = {kNegInf, 0.f};
+  if (tid < n_splits) ml = *reinterpret_cast<const f32x2*>(ws_ml + (slot0 + tid) * 2);
   const int n = min(n_splits, len > 0 ? (len + split_keys - 1) / split_keys : 0);
-  const size_t slot0 = ((size_t)b * H + h) * n_splits;
+  if (n <= 1) return;  // empty or finished by the split kernel
+  const bool active = tid < n;
+  const float m_t = active ? ml[0] : kNegInf;
+  const float wmax = wave_max(m_t);
+  if (lane == 0) sm_red[0][wave] = wmax;
+  __syncthreads();
+  const float Mg = fmaxf(fmaxf(sm_red[0][0], sm_red[0][1]), fmaxf(sm_red[0][2], sm_red[0][3]));
+  const float f = active ? exp2_hw(m_t - Mg) : 0.f;
+  const float wl = wave_sum(active ? f * ml[1] : 0.f);
+  sm_f[tid] = f;
+  if (lane == 0) sm_red[1][wave] = wl;
+  __syncthreads();
 
-  float M = kNegInf;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, ws_ml[(slot0 + s) * 2]);
-  M = wave_max(M);
-  float Lp = 0.f;
-  for (int s = lane; s < n; s += 64)
-    Lp = __builtin_fmaf(exp2_hw(ws_ml[(slot0 + s) * 2] - M), ws_ml[(slot0 + s) * 2 + 1], Lp);
-  const float L = wave_sum(Lp);
-
+  // wave w sums chunks w, w+4, w+8, ... for dims 2*lane, 2*lane+1
   const int d0 = 2 * lane;
-  const bool has_d = d0 < D;
-  float U0 = 0.f, U1 = 0.f;
-  for (int c0 = 0; c0 < n; c0 += 64) {
-    const int s_l = c0 + lane;
-    const float f_l = s_l < n ? exp2_hw(ws_ml[(slot0 + s_l) * 2] - M) : 0.f;
-    const int cnt = min(64, n - c0);
+  float G0 = 0.f, G1 = 0.f;
+  if (d0 < D) {
 #pragma unroll 8
-    for (int j = 0; j < cnt; ++j) {
-      const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f_l), j));
-      if (has_d) {
-        const f32x2 w = *reinterpret_cast<const f32x2*>(ws_u + (slot0 + c0 + j) * D + d0);
-        U0 = __builtin_fmaf(f, w[0], U0);
-        U1 = __builtin_fmaf(f, w[1], U1);
-      }
+    for (int t = wave; t < n; t += 4) {
+      const f32x2 w = *reinterpret_cast<const f32x2*>(ws_u + (slot0 + t) * D + d0);
+      G0 = __builtin_fmaf(sm_f[t], w[0], G0);
+      G1 = __builtin_fmaf(sm_f[t], w[1], G1);
     }
+    sm_part[wave][d0] = G0;
+    sm_part[wave][d0 + 1] = G1;
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  const size_t orow = ((size_t)b * H + h) * D;
-  if (has_d) *reinterpret_cast<uint32_t*>(O + orow + d0) = pack_bf16x2(U0 * inv, U1 * inv);
-  if (lane == 0) LSE[(size_t)b * H + h] = L > 0.f ? (M + log2_hw(L)) * kLn2 : kNegInf;
+  __syncthreads();
+  if (wave == 0) {
+    const float Lg = sm_red[1][0] + sm_red[1][1] + sm_red[1][2] + sm_red[1][3];
+    const float inv = 1.f / Lg;
+    if (d0 < D) {
+      const float o0 = sm_part[0][d0] + sm_part[1][d0] + sm_part[2][d0] + sm_part[3][d0];
+      const float o1 = sm_part[0][d0 + 1] + sm_part[1][d0 + 1] + sm_part[2][d0 + 1] + sm_part[3][d0 + 1];
+      *reinterpret_cast<uint32_t*>(O + bh * D + d0) = pack_bf16x2(o0 * inv, o1 * inv);
+    }
+    if (lane == 0) LSE[bh] = (Mg + log2_hw(Lg)) * kLn2;
+  }
 }
 
 template <int D>
 hipError_t launch(const DecodeArgs& a) {
   const float c = a.scale * kLog2e;
   float* ws_u = a.ws;
-  float* ws_ml = a.ws + (size_t)a.B * a.H * a.n_splits * D;
+  float* ws_ml = ws_u + (size_t)a.B * a.H * a.n_splits * D;
   {
     void* args[] = {(void*)&a.q, (void*)&a.kcache, (void*)&a.vcache, (void*)&a.seqlens,
-                    (void*)&a.offsets, (void*)&ws_u, (void*)&ws_ml, (void*)&a.H,
-                    (void*)&a.split_keys, (void*)&a.n_splits, (void*)&c};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<D>),
-                                   dim3((unsigned)a.H, (unsigned)a.n_splits, (unsigned)a.B),
-                                   dim3(kThreads), args, 0, a.stream);
+                    (void*)&a.offsets, (void*)&a.o, (void*)&a.lse, (void*)&ws_u, (void*)&ws_ml,
+                    (void*)&a.H, (void*)&a.split_keys, (void*)&a.n_splits, (void*)&c};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<D>),
+                                         dim3((unsigned)a.H, (unsigned)a.n_splits, (unsigned)a.B),
+                                         dim3(kThreads), args, 0, a.stream);
     if (e != hipSuccess) return e;
   }
+  if (a.n_splits == 1) return hipSuccess;  // every sequence finished in the split kernel
   void* args[] = {(void*)&ws_u, (void*)&ws_ml, (void*)&a.seqlens, (void*)&a.o, (void*)&a.lse,
                   (void*)&a.H, (void*)&a.split_keys, (void*)&a.n_splits};
   return hipLaunchKernel(reinterpret_cast<const void*>(&decode_merge_kernel<D>),
-                         dim3((unsigned)a.H, (unsigned)a.B), dim3(64), args, 0, a.stream);
+                         dim3((unsigned)a.H, (unsigned)a.B), dim3(kThreads), args, 0, a.stream);
 }
 
 }  // namespace

@@ -93,7 +93,7 @@ def test_decode_rejects_invalid_arguments():
     assert dec_call(scale=float("nan")) == INVALID
     assert dec_call(split_keys=-64) == INVALID
     assert dec_call(split_keys=100) == INVALID  # not a multiple of 64
-    assert dec_call(split_keys=64, max_seqlen=64 * 65536, ws_bytes=1 << 40) == INVALID  # > 65535 chunks
+    assert dec_call(split_keys=64, max_seqlen=64 * 257, ws_bytes=1 << 40) == INVALID  # > 256 chunks
     assert dec_call(d=96) == UNSUPPORTED
     assert dec_call(ws=None) == WORKSPACE
     assert dec_call(ws=A + 8) == WORKSPACE
@@ -109,6 +109,8 @@ def test_workspace_and_split_plan():
     sk = fa.fa_decode_split_keys(64, 32, 128, 16384)
     assert sk % 64 == 0 and 64 * 32 * -(-16384 // sk) <= 32768
     assert fa.fa_decode_workspace_bytes(3, 5, 64, 1000, 128) == 3 * 5 * 8 * 66 * 4
+    # at most 256 chunks per sequence
+    assert -(-(1 << 24) // fa.fa_decode_split_keys(1, 1, 128, 1 << 24)) <= 256
     assert fa.fa_decode_workspace_bytes(0, 5, 64, 1000, 128) == 0
     assert fa.fa_decode_workspace_bytes(3, 5, 96, 1000, 128) == 0
 

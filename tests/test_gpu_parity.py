@@ -228,3 +228,18 @@ def test_decode_matches_fwd_single_query(fa):
         of, lf = run_fwd(fa, qb, kb, vb, 0.088, False)
         assert (lf[0, :, 0] - lse[b]).abs().max().item() <= 1e-4
         assert (of[0, :, 0].float() - o[b].float()).abs().max().item() <= 2e-2
+
+
+def test_decode_workspace_reused_across_calls(fa):
+    """One workspace serves consecutive calls with different inputs."""
+    log("case decode workspace reuse")
+    lens = [700, 64, 3000, 1]
+    B, H, d = len(lens), 4, 128
+    ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, d, max(lens), 256), dtype=torch.uint8,
+                     device="cuda")
+    for call in range(3):
+        q, kc, vc, sl, off = W.decode_inputs(B, H, d, lens, seed=100 + call, device="cuda")
+        o, lse = fa.fa_decode_varlen(q, kc, vc, sl, off, max(lens), 0.088, 256, workspace=ws)
+        torch.cuda.synchronize()
+        O, L = oracle.decode(q, kc, vc, sl.cpu(), off.cpu(), 0.088)
+        check(o, lse, O, L, TOL_BF16, f"reuse call {call}")
