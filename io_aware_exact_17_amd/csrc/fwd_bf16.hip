@@ -11,36 +11,44 @@
 // probability tiles live only in registers.  Key tiles wholly above the
 // causal diagonal are never loaded (explainer §6).
 //
-// Mapping to CDNA4:
-//  * 8 waves x 32 query rows = 256 rows per workgroup, one workgroup per CU,
-//    two waves per SIMD.  Both products run on the matrix cores as
-//    v_mfma_f32_32x32x16_bf16.
-//  * The score tile is formed transposed, S^T = K Q^T, so every lane holds
+// Mapping to CDNA4 (head dimension 128; d = 64 runs fwd_bf16_d64.hip):
+//  * 4 waves x 64 query rows = 256 rows per workgroup, one workgroup (one wave
+//    per SIMD) per CU.  A wave holds its rows as two 32-row blocks and both
+//    products run on the matrix cores as v_mfma_f32_32x32x16_bf16; every K or
+//    V operand read from LDS feeds both row blocks, which halves the LDS read
+//    traffic per matrix instruction against 32-row waves.  O^T lives in the
+//    accumulation registers, and so does Q (loaded there directly).
+//  * The score block is formed transposed, S^T = K Q^T, so every lane holds
 //    one query column: row max and row sum are in-lane reductions plus one
 //    exchange between lane halves (v_permlane32_swap); no reduction crosses
-//    waves.  The S^T accumulators, rounded to bf16, are directly the B operand
-//    of O^T += V^T P^T, so P never leaves registers.
-//  * Two wave groups in opposite phase.  Waves 0-3 (group A) handle each key
-//    tile as  S = K Q^T -> softmax -> O += P V;  waves 4-7 (group B, one on
-//    each SIMD next to a group-A wave) as  O += P V of the previous tile ->
-//    S = K Q^T -> softmax.  After each barrier the two waves sharing a SIMD
-//    therefore run their vector-ALU softmax while the other one feeds the
-//    matrix core, instead of both waiting on the same unit.
-//  * K tiles are staged row-major in LDS; V tiles transposed (V^T, keys
-//    contiguous) with the key order permuted inside each group of 16 so that
-//    one 16-byte LDS read yields exactly the 8 keys a lane's P registers hold.
-//    Row strides are padded by 16 bytes (no bank conflicts).  Two K buffers
-//    and three V^T buffers (group B reads the previous V tile); one barrier
-//    per tile.  The tile after the next is fetched from HBM into registers
-//    with 16-byte loads a whole tile ahead: waves 0-3 move V tiles
-//    (transposing them in registers), waves 4-7 move K tiles.
-//  * exp is 2^x on v_exp_f32 with log2(e) folded into the scale.  The
-//    reference maximum is not recomputed per tile: P is formed against the
-//    current reference and only when a tile's P sum exceeds 2^8 (so some P
-//    could exceed 256 before rounding to bf16) is the exact row maximum
-//    taken, the reference moved and the output accumulator rescaled.  That
-//    happens on the first tile and rarely afterwards; the mathematics is
-//    unchanged because the final division uses the same reference.
+//    waves.  The S^T products are single-instruction inline assembly so the
+//    scores land in vector registers, where the softmax reads them.  Rounded
+//    to bf16 they are directly the B operand of O^T += V^T P^T, so P never
+//    leaves registers.
+//  * K and V tiles (64 keys) go from HBM straight into LDS
+//    (global_load_lds_dwordx4, 1 KB per wave instruction, no staging
+//    registers), both row-major, with the 16-byte chunks of each row permuted
+//    by an XOR of a function of the row index so that both kinds of operand
+//    read below touch 16 distinct 16-byte bank groups per 256 bytes.  The V^T
+//    operand comes from the row-major V tile through the transposing LDS read
+//    ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
+//    element i%4 of the 8-byte pieces addressed by lanes i0 + (i%16)/4 + 4k,
+//    k = 0..3, so addresses are chosen such that a lane receives, for its own
+//    output dim, the four keys its P registers hold.  Four LDS buffers per
+//    operand; K tiles are requested four tiles ahead, V tiles three, and
+//    waited for explicitly; one barrier per 64 keys.
+//  * Software pipeline over 32-key blocks inside each wave: while the scores
+//    of block b go through the softmax on the vector ALUs, the matrix cores
+//    compute the scores of block b+1 and add block b-1's P V into O.  A step
+//    is four quarters, each with four S^T and four P V instructions, eight
+//    scores of softmax and the LDS reads for the next quarter issued first.
+//  * exp is 2^x on v_exp_f32 with log2(e) folded into the scale.  P is formed
+//    against the current reference maximum; only when a block's P sum per
+//    lane exceeds 2^8 (so some P could exceed 256 before rounding to bf16) is
+//    the exact row maximum taken, the reference moved and O and l rescaled.
+//    The mathematics is unchanged: the final division uses the same
+//    reference.  Masks (causal diagonal, keys past the end) act on P, so they
+//    are exact whatever the sign of the scale.
 //  * Workgroups are issued heaviest query tile first; consecutive workgroup
 //    ids walk the heads, so when B*H is a multiple of 8 every tile of a head
 //    lands on the same XCD (workgroups are dealt round-robin to the 8 XCDs)
@@ -52,54 +60,150 @@ namespace fa {
 
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kMovers = 256;      // threads staging each operand
-constexpr int kBR = 256;          // query rows per workgroup (8 waves x 32)
-constexpr int kKBuf = 2;          // LDS K buffers
-constexpr int kVBuf = 3;          // LDS V^T buffers
-constexpr float kSumBound = 256.f;  // a tile's P sum per lane half stays <= 2^8
-constexpr int kPrefetch = 6;      // LDS operand reads kept ahead of the matrix cores
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kBR = 256;             // query rows per workgroup (4 waves x 64)
+constexpr int kBC = 64;              // keys per staged tile (two 32-key blocks)
+constexpr int kNBuf = 4;             // LDS buffers per operand
+constexpr float kSumBound = 256.f;   // a block's P sum per lane stays <= 2^8
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BC = 8192 / D;    // keys per tile: 64 for d=128, 128 for d=64
-  static constexpr int KS = D / 16;      // k-steps of S^T = K Q^T
-  static constexpr int NKB = BC / 32;    // 32-key blocks per tile
-  static constexpr int NDB = D / 32;     // 32-row blocks of O^T
-  static constexpr int KROW = D + 8;     // LDS row stride of K (elements)
-  static constexpr int VROW = BC + 8;    // LDS row stride of V^T (elements)
-  static constexpr int KTILE = BC * KROW;
-  static constexpr int VTILE = D * VROW;
-  static constexpr int KCHUNKS = BC * D / 8 / kMovers;   // 16-byte K chunks per K mover
-  static constexpr int VBLOCKS = (BC / 4) * (D / 8);     // 4-key x 8-dim V blocks per tile
-  static constexpr int LDS_ELEMS = kKBuf * KTILE + kVBuf * VTILE;
-  static_assert(KCHUNKS == 4 && KCHUNKS * kMovers * 8 == BC * D, "K tile split");
-  static_assert(VBLOCKS == kMovers, "one V block per V mover");
+  static constexpr int KS = D / 16;         // k-steps of S^T = K Q^T
+  static constexpr int NDB = D / 32;        // 32-row blocks of O^T
+  static constexpr int CPR = D / 8;         // 16-byte chunks per row
+  static constexpr int TILE = kBC * D;      // elements per K or V tile
+  static constexpr int RPI = 64 / CPR;      // tile rows per 1 KB wave instruction
+  static constexpr int IPT = kBC / RPI;     // wave instructions per tile
+  static constexpr int IPW = IPT / kWaves;  // ... per wave
+  static_assert(IPW * kWaves == IPT, "tile loads split evenly over the waves");
 };
 
-// Position of a group of four keys inside its group of 16 in the V^T layout:
-// the two middle groups are swapped, so positions 8h..8h+7 hold keys
-// {4h..4h+3, 8+4h..8+4h+3} — the keys accumulator registers 0..7 of lane
-// half h cover in the S^T layout.
-__device__ __forceinline__ int vt_pos4(int group4) {
-  return ((group4 & 1) << 1) | ((group4 >> 1) & 1);
+// LDS slot of 16-byte chunk c of tile row r: c ^ f(r).  With 256-byte bank
+// lines, f maps the 16 rows of an aligned group to distinct values (K reads:
+// 16 lanes, one chunk of 16 rows) and gives the 4 rows of an aligned group of
+// four distinct high bits (transposing V reads: 4 rows x 4 chunks).
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (D == 128) {
+    return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  } else {  // two 128-byte rows per bank line; bit 0 of r picks the half
+    return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
 }
 
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// One 16-byte-per-lane copy from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l's 16 bytes at gbase + voff land at LDS
+// byte lds_addr + 16 l.  Issued from inline assembly so that the compiler
+// does not tie later LDS reads to it with waits of its own: the kernel waits
+// for these copies explicitly (vmcnt, then a barrier) before reading a tile.
+__device__ __forceinline__ void copy_to_lds(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds_addr)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// One k-step of S^T = K Q^T on the matrix core (v_mfma_f32_32x32x16_bf16)
+// written as a single instruction, so that the scores land in vector
+// registers, where the softmax reads them, while the Q operand stays in
+// accumulation registers.  The compiler does not see these as matrix
+// instructions, so the code orders them: a chain alternates its two row
+// blocks (as compiled chains do), and the first vector-ALU read of a score
+// comes three matrix instructions or a wait (products_done) after the last
+// instruction of its chain.
+__device__ __forceinline__ void qk_first(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void qk_next(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// 16 bytes from global memory into four accumulation registers.  The
+// compiler does not track this load; the caller waits for it (vmcnt).
+__device__ __forceinline__ bf16x8 load_to_acc(const bf16* p) {
+  bf16x8 r;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(r) : "v"(p) : "memory");
+  return r;
+}
+
+// Scheduling pattern: N matrix instructions, each followed by its share of
+// the transcendental (TRANS) and other vector (VALU) instructions; the
+// first TRANS % N and VALU % N shares are one larger.
+template <int N, int TRANS, int VALU, int I = 0>
+__device__ __forceinline__ void mfma_valu_pattern() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr ((TRANS + N - 1 - I) / N > 0)
+      __builtin_amdgcn_sched_group_barrier(0x400, (TRANS + N - 1 - I) / N, 0);
+    if constexpr ((VALU + N - 1 - I) / N > 0)
+      __builtin_amdgcn_sched_group_barrier(0x002, (VALU + N - 1 - I) / N, 0);
+    mfma_valu_pattern<N, TRANS, VALU, I + 1>();
+  }
+}
+
+// The rare paths replace the P pairs and row sums of the common path; they
+// consume them first, so that the compiler cannot sink the common-path
+// softmax out of the matrix-core quarters into the branch that keeps it.
+__device__ __forceinline__ void consume(const uint32_t (&pk)[2][8], const float (&lsum)[2]) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[rb][i]));
+    asm volatile("" ::"v"(lsum[rb]));
+  }
+}
+
+// 32 wait states: more than the matrix-instruction-to-vector-ALU distance
+// an 8-pass product needs before its result may be read.  Used where a
+// vector read of a product's result could follow it closely: after the
+// first scores, before the rare rescale of O and before the epilogue.  In
+// the steady state the fixed order of each quarter keeps at least three
+// matrix instructions between the last product into a score register and
+// its first read (next step), so no wait is needed there.
+__device__ __forceinline__ void products_done() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n\ts_nop 15");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Matrix-core operands of one quarter step, read from LDS one quarter ahead.
+template <int D>
+struct QuarterOps {
+  bf16x8 k[D / 64];  // K operands of k-steps 2q', 2q'+1 (d=128) or q' (d=64)
+  bf16x8 v[D / 64];  // V^T operands of dim blocks (q'%2)*NDB/2 + i
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int Nq, int Nk,
-    float c, int negate_q, int n_qtiles) {
+    float c, int n_qtiles) {
   using C = FwdCfg<D>;
-  constexpr int BC = C::BC;
-  __shared__ __attribute__((aligned(16))) bf16 smem[C::LDS_ELEMS];
-  bf16* const sK = smem;                      // kKBuf K tiles
-  bf16* const sV = smem + kKBuf * C::KTILE;   // kVBuf V^T tiles
+  using Ops = QuarterOps<D>;
+  constexpr int TB = C::TILE * 2;        // bytes per K or V tile
+  constexpr int VREG = kNBuf * TB;       // byte offset of the V buffers
+  constexpr int ROWB = D * 2;            // bytes per tile row
+  constexpr int KQ = C::KS / 4;          // k-steps per quarter
+  constexpr int VQ = C::NDB / 2;         // dim blocks per quarter
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * kNBuf * C::TILE];
+  lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const bool group_b = wave >= 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;   // query column of this lane in S^T / O^T
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group this lane holds
 
@@ -112,237 +216,462 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const size_t kbase = (size_t)bh * Nk * D;
 
   const int kv_end = CAUSAL ? min(Nk, q0 + kBR + off) : Nk;
-  const int n_tiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  const int n_tiles = kv_end > 0 ? (kv_end + kBC - 1) / kBC : 0;
 
-  const int wq0 = q0 + wave * 32;  // first query row of this wave
-  const int qi = wq0 + col;        // this lane's query row
-  const int kv_end_w = CAUSAL ? min(Nk, wq0 + 32 + off) : Nk;
-  const int nt_w = kv_end_w > 0 ? (kv_end_w + BC - 1) / BC : 0;  // tiles this wave needs
+  const int wq0 = q0 + wave * 64;  // first query row of this wave
+  const int qi0 = wq0 + col;       // this lane's row in row block 0 (+32 in block 1)
+  const int kv_end_w = CAUSAL ? min(Nk, wq0 + 64 + off) : Nk;
+  const int nbw = kv_end_w > 0 ? (kv_end_w + 31) / 32 : 0;  // 32-key blocks this wave needs
+  const int njw = (nbw + 1) / 2;                             // tiles this wave needs
 
-  // Q^T operand: lane holds Q[qi][16s + 8*half + 0..7].  Rows past Nq read
-  // row Nq-1 (their results are never stored).
-  bf16x8 qf[C::KS];
-  {
-    const uint32_t flip = negate_q ? 0x80008000u : 0u;  // exact sign flip for a negative scale
-    const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)min(qi, Nq - 1) * D);
+  // Q^T operands: lane holds Q[row][16s + 8*half + 0..7] of both row blocks.
+  // Rows past Nq read row Nq-1 (their results are never stored).
+  // They are loaded straight into accumulation registers, where only the
+  // S^T products read them; the first wait on vector memory (before the
+  // first barrier) covers these loads.
+  bf16x8 qf[2][C::KS];
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      u32x4 w = src[2 * s + half];
-      w ^= flip;
-      qf[s] = __builtin_bit_cast(bf16x8, w);
-    }
+  for (int rb = 0; rb < 2; ++rb) {
+    const bf16* src = Q + qbase + (size_t)min(qi0 + 32 * rb, Nq - 1) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) qf[rb][s] = load_to_acc(src + 16 * s);
   }
 
   // ---------------------------------------------------------- tile staging
-  // Waves 0-3 move V, waves 4-7 move K, four 16-byte chunks per thread.
-  //   K mover mt: chunks mt + 256 i of the row-major tile, i.e. key
-  //     mt / (D/8) + (256 / (D/8)) i, 8 dims at (mt % (D/8)) * 8.
-  //   V mover mt: keys 4*vkg .. 4*vkg+3 of dims vdb*8 .. vdb*8+7, written to
-  //     V^T transposed.
-  const bool k_mover = tid >= kMovers;
-  const int mt = tid & (kMovers - 1);
-  constexpr int kKeysPerPass = kMovers / (D / 8);
-  const int vkg = mt % (BC / 4);
-  const int vdb = mt / (BC / 4);
-  const int first_key = k_mover ? mt / (D / 8) : 4 * vkg;
-  const int key_step = k_mover ? kKeysPerPass : 1;
-  const int dcol = k_mover ? (mt % (D / 8)) * 8 : vdb * 8;
-  u32x4 stg[4];
-
-  // The tile base is uniform, so loads take an SGPR base plus a 32-bit lane
-  // byte offset.  Keys past Nk read row Nk-1 instead: finite values whose
-  // scores are masked to -inf, so they carry zero weight.
-  auto load_tile = [&](int j) {
-    const int k0 = j * BC;
-    const char* base = reinterpret_cast<const char*>((k_mover ? K : V) + kbase + (size_t)k0 * D);
-    const int last = Nk - 1 - k0;
+  // Wave w issues wave instructions w*IPW .. w*IPW+IPW-1 of a tile; wave
+  // instruction ii fills tile rows ii*RPI .. ii*RPI+RPI-1 (1 KB, lane l at
+  // byte 16 l), so lane l owns slot l%CPR of row ii*RPI + l/CPR and fetches
+  // the chunk that slot holds.  Full tiles use a uniform tile address plus a
+  // fixed lane offset; in a tile that crosses Nk, rows past Nk fetch row
+  // Nk-1 (finite values whose P is masked to 0).
+  const int ld_row = lane / C::CPR;
+  const int ld_slot = lane % C::CPR;
+  uint32_t g_off[C::IPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(first_key + key_step * i, last);
-      stg[i] = *reinterpret_cast<const u32x4*>(base + (uint32_t)((key * D + dcol) * 2));
-    }
-  };
-  auto store_tile = [&](int j) {
-    if (k_mover) {
-      bf16* sk = sK + (j % kKBuf) * C::KTILE;
+  for (int i = 0; i < C::IPW; ++i) {
+    const int r = (wave * C::IPW + i) * C::RPI + ld_row;
+    g_off[i] = (uint32_t)(r * ROWB + swz<D>(r, ld_slot) * 16);  // the permutation is its own inverse
+  }
+  const char* const kg = reinterpret_cast<const char*>(K + kbase);
+  const char* const vg = reinterpret_cast<const char*>(V + kbase);
+  const uint32_t lds_wave = (uint32_t)(size_t)lds + wave * C::IPW * 1024;
+  auto issue = [&](const char* base, int region, int j) {
+    const char* t = base + (size_t)j * TB;
+    const uint32_t dst = lds_wave + region;
+    if ((j + 1) * kBC <= Nk) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(sk + (first_key + key_step * i) * C::KROW + dcol) = stg[i];
+      for (int i = 0; i < C::IPW; ++i) copy_to_lds(t, g_off[i], dst + i * 1024);
     } else {
-      bf16* sv = sV + (j % kVBuf) * C::VTILE;
-      // 4 keys x 8 dims -> 8 rows of V^T, 4 keys each.
-      const int pos = 16 * (vkg >> 2) + 4 * vt_pos4(vkg & 3);
+      const int last = Nk - 1 - j * kBC;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t e01 = __builtin_amdgcn_perm(stg[1][i], stg[0][i], 0x05040100u);
-        const uint32_t e23 = __builtin_amdgcn_perm(stg[3][i], stg[2][i], 0x05040100u);
-        const uint32_t o01 = __builtin_amdgcn_perm(stg[1][i], stg[0][i], 0x07060302u);
-        const uint32_t o23 = __builtin_amdgcn_perm(stg[3][i], stg[2][i], 0x07060302u);
-        *reinterpret_cast<u32x2*>(sv + (vdb * 8 + 2 * i) * C::VROW + pos) = u32x2{e01, e23};
-        *reinterpret_cast<u32x2*>(sv + (vdb * 8 + 2 * i + 1) * C::VROW + pos) = u32x2{o01, o23};
+      for (int i = 0; i < C::IPW; ++i) {
+        const int r = (wave * C::IPW + i) * C::RPI + ld_row;
+        copy_to_lds(t, (uint32_t)(min(r, last) * ROWB + swz<D>(r, ld_slot) * 16), dst + i * 1024);
       }
     }
   };
+  // Tile j of K and of V both go to buffer j % kNBuf.
+  auto issue_k = [&](auto buf, int j) { issue(kg, decltype(buf)::value * TB, j); };
+  auto issue_v = [&](auto buf, int j) { issue(vg, VREG + decltype(buf)::value * TB, j); };
 
-  // ------------------------------------------------------ per-tile stages
-  f32x16 oacc[C::NDB];
+  // LDS read offsets for buffer 0, first 32-key half of the tile; the
+  // buffer, the half and (for V) the 16-key group are immediate offsets,
+  // since the row permutation depends on the row index modulo 16 only.
+  //   K operand of k-step s: key row col, chunk 2s + half.
+  //   V^T operand (transposing read cc of dim block db): lane l addresses key
+  //   8cc + 4*half + (l%16)/4 and dims d..d+3, d = 32db + 16*((l/16)%2) + 4*(l%4).
+  uint32_t k_off[C::KS];
 #pragma unroll
-  for (int i = 0; i < C::NDB; ++i) oacc[i] = f32x16{};
-  float m_ref = kNegInf;  // reference maximum, log2 units (score * c)
-  float l_part = 0.f;     // this lane half's share of the row sum
-  f32x16 sacc[C::NKB];
-  uint32_t pk[C::NKB][8];  // bf16 P pairs of the latest softmax
+  for (int s = 0; s < C::KS; ++s) k_off[s] = (uint32_t)(col * ROWB + swz<D>(col, 2 * s + half) * 16);
+  uint32_t v_off[2][C::NDB];
+  {
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int key = 8 * cc + 4 * half + ((lane & 15) >> 2);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const int d = 32 * db + tr_dim;
+        v_off[cc][db] = (uint32_t)(VREG + key * ROWB + swz<D>(key, d >> 3) * 16 + (d & 7) * 2);
+      }
+    }
+  }
 
-  // Matrix-core loops keep kPrefetch LDS operand reads in flight: the
-  // schedule is pinned to  kPrefetch reads, then (1 MFMA, 1 read) pairs,
-  // then the remaining MFMAs, so no MFMA waits on a read issued just before.
-  auto pipeline_schedule = [&](auto n_mfma) {
-    constexpr int N = decltype(n_mfma)::value;
+  // Operands of quarter q of a step whose scores come from half HB of K
+  // buffer KB and whose P V uses half HB of V buffer VB: the K operands of
+  // k-steps q*KQ .. q*KQ+KQ-1 and the V^T operands of the keys
+  // 32*HB + 16*(q/2) + {4h..4h+3, 8+4h..8+4h+3} for dim blocks
+  // (q%2)*VQ .. (q%2)*VQ+VQ-1.
+  auto load_ops = [&](auto kb, auto vb, auto hb, auto qq) {
+    constexpr int Q4 = decltype(qq)::value;
+    constexpr int KOFF = decltype(kb)::value * TB + decltype(hb)::value * 32 * ROWB;
+    constexpr int VOFF = decltype(vb)::value * TB + (decltype(hb)::value * 32 + 16 * (Q4 >> 1)) * ROWB;
+    Ops o;
 #pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < KQ; ++i)
+      o.k[i] = *reinterpret_cast<const lds_bf16x8*>(lds + k_off[Q4 * KQ + i] + KOFF);
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + kPrefetch < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < VQ; ++i) {
+      const int db = (Q4 & 1) * VQ + i;
+      const u32x2 lo = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + v_off[0][db] + VOFF)));
+      const u32x2 hi = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + v_off[1][db] + VOFF)));
+      o.v[i] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+    return o;
+  };
+
+  // ------------------------------------------------------ per-block stages
+  f32x16 oacc[2][C::NDB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int i = 0; i < C::NDB; ++i) oacc[rb][i] = f32x16{};
+  float m_ref[2] = {kNegInf, kNegInf};  // reference maximum per row block, log2 units
+  float l_part[2] = {0.f, 0.f};         // this lane half's share of the row sums
+
+  f32x16 sA[2], sB[2];          // S^T accumulators: even / odd blocks
+  uint32_t pA[2][8], pB[2][8];  // bf16 P pairs: even / odd blocks
+
+  // Block b needs a mask when it reaches past Nk or, causally, past the
+  // wave's first query (blocks past the wave's last key are masked whole;
+  // their K may be stale).  Accumulator register r of lane half h holds key
+  // 32b + 4h + 8(r/4) + r%4; it is visible to row block rb iff that key is
+  // <= lim(rb), i.e. iff 8(r/4) + r%4 <= lim(rb) - 32b - 4h.
+  auto needs_mask = [&](int b) {
+    return (32 * b + 32 > Nk) || (CAUSAL && 32 * b + 31 > wq0 + off);
+  };
+  auto mask_room = [&](int b, int rb) {
+    const int lim = CAUSAL ? min(Nk - 1, qi0 + 32 * rb + off) : Nk - 1;
+    return lim - 32 * b - 4 * half;
+  };
+
+  // P = 2^(s*c - m) against the current reference (0 where masked) for
+  // accumulator registers R0 .. R0+7 of a row block: bf16 pairs for the
+  // matrix core, fp32 sum for l.
+  // The eight values are independent until the final sum, and are written
+  // stage by stage (all fma, all exp, pack, tree sum) so that in-order
+  // issue never waits on one value's chain while matrix work is queued.
+  auto exp8 = [&](auto masked, auto r0, const f32x16& s, float m_use, int room, uint32_t (&pk)[8],
+                  float& lsum) {
+    constexpr int R0 = decltype(r0)::value;
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = __builtin_fmaf(s[R0 + i], c, -m_use);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = exp2_hw(p[i]);
+    if constexpr (decltype(masked)::value) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = R0 + i;
+        p[i] = (8 * (r >> 2) + (r & 3) > room) ? 0.f : p[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) pk[(R0 + i) >> 1] = pack_bf16x2(p[i], p[i + 1]);
+    lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  };
+  using R0c = std::integral_constant<int, 0>;
+  using R8c = std::integral_constant<int, 8>;
+
+  // A block whose P sum in some lane exceeds 2^8 (or is not finite: m = -inf
+  // before the first visible key) takes the exact path: row maximum over the
+  // visible keys, moved reference, l and O rescaled (O then holds the P V of
+  // the blocks before b), P recomputed.  Every P then stays <= 2^8.
+  auto fixup = [&](int b, const f32x16 (&sacc)[2], uint32_t (&pk)[2][8], float (&lsum)[2]) {
+    if (wave_any(!(lsum[0] <= kSumBound) || !(lsum[1] <= kSumBound))) {
+      consume(pk, lsum);
+      products_done();  // O is read below
+      const bool masked = needs_mask(b);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int room = masked ? mask_room(b, rb) : 31;
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          mx = (8 * (r >> 2) + (r & 3) > room) ? mx : fmaxf(mx, sacc[rb][r] * c);
+        mx = max_across_halves(mx);
+        const float m_new = fmaxf(m_ref[rb], mx);
+        const float alpha = m_new != m_ref[rb] ? exp2_hw(m_ref[rb] - m_new) : 1.f;  // 0 from -inf
+        l_part[rb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::NDB; ++i) oacc[rb][i] *= alpha;
+        // The next products into O are inline assembly the compiler does not
+        // see: give the rescaled accumulators their wait states here.
+        asm volatile("s_nop 7" ::: "memory");
+        m_ref[rb] = m_new;
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        lsum[rb] = 0.f;
+        exp8(std::true_type{}, R0c{}, sacc[rb], m_use, room, pk[rb], lsum[rb]);
+        exp8(std::true_type{}, R8c{}, sacc[rb], m_use, room, pk[rb], lsum[rb]);
+      }
+    }
+    l_part[0] += lsum[0];
+    l_part[1] += lsum[1];
+  };
+
+  // Quarter Q4 of a pipeline step around block b: the k-steps 2q, 2q+1 of
+  // the scores of block b+1 (into s_nxt), the dim blocks 2(q%2), 2(q%2)+1 of
+  // the P V of block b-1 for the keys of P pair group q/2, and eight of
+  // block b's P values (row block q/2, registers 8(q%2)..8(q%2)+7).  The
+  // three streams are independent; the instruction order is fixed here, as
+  // eight groups of one matrix instruction and its share of the softmax:
+  //   1 S(rb0,2q)  fma x4      2 PV(db0,rb0) fma x4
+  //   3 S(rb1,2q)  exp x2      4 PV(db0,rb1) exp x2
+  //   5 S(rb0,2q+1) exp x2, pack   6 PV(db1,rb0) exp x2, pack, add
+  //   7 S(rb1,2q+1) pack, add x2   8 PV(db1,rb1) pack, add x5
+  // Each exp result is read two groups later at the earliest (the one
+  // wait state a transcendental result needs is always covered).
+  auto quarter = [&](auto qq, const Ops& o, f32x16 (&s_nxt)[2], const f32x16 (&s_cur)[2],
+                     uint32_t (&p_cur)[2][8], const uint32_t (&p_prv)[2][8], float (&lsum)[2]) {
+    constexpr int Q4 = decltype(qq)::value;
+    constexpr int RB = Q4 >> 1;
+    constexpr int T = Q4 >> 1;
+    constexpr int R0 = (Q4 & 1) * 8;
+    constexpr int S0 = 2 * Q4;  // k-steps S0, S0+1
+    constexpr int DB0 = (Q4 & 1) * 2;
+    static_assert(D == 128, "explicit quarter schedule is written for d = 128");
+    const bf16x8 b0 = __builtin_bit_cast(
+        bf16x8, u32x4{p_prv[0][4 * T], p_prv[0][4 * T + 1], p_prv[0][4 * T + 2], p_prv[0][4 * T + 3]});
+    const bf16x8 b1 = __builtin_bit_cast(
+        bf16x8, u32x4{p_prv[1][4 * T], p_prv[1][4 * T + 1], p_prv[1][4 * T + 2], p_prv[1][4 * T + 3]});
+    const f32x16& x = s_cur[RB];
+    const float nm = -m_ref[RB];
+    float p0, p1, p2, p3, p4, p5, p6, p7, t0, t1, t2, t3;
+    uint32_t k0, k1, k2, k3;
+#define FA_FMA(d, a) "v_fma_f32 " d ", " a ", %[c], %[nm]\n\t"
+    // 1
+    if constexpr (S0 == 0) {
+      asm volatile("v_mfma_f32_32x32x16_bf16 %[s], %[a], %[b], 0\n\t"
+                   FA_FMA("%[p0]", "%[x0]") FA_FMA("%[p1]", "%[x1]") FA_FMA("%[p2]", "%[x2]") FA_FMA("%[p3]", "%[x3]")
+                   : [s] "=&v"(s_nxt[0]), [p0] "=&v"(p0), [p1] "=&v"(p1), [p2] "=&v"(p2), [p3] "=&v"(p3)
+                   : [a] "v"(o.k[0]), [b] "a"(qf[0][S0]), [x0] "v"(x[R0]), [x1] "v"(x[R0 + 1]),
+                     [x2] "v"(x[R0 + 2]), [x3] "v"(x[R0 + 3]), [c] "s"(c), [nm] "v"(nm));
+    } else {
+      asm volatile("v_mfma_f32_32x32x16_bf16 %[s], %[a], %[b], %[s]\n\t"
+                   FA_FMA("%[p0]", "%[x0]") FA_FMA("%[p1]", "%[x1]") FA_FMA("%[p2]", "%[x2]") FA_FMA("%[p3]", "%[x3]")
+                   : [s] "+v"(s_nxt[0]), [p0] "=&v"(p0), [p1] "=&v"(p1), [p2] "=&v"(p2), [p3] "=&v"(p3)
+                   : [a] "v"(o.k[0]), [b] "a"(qf[0][S0]), [x0] "v"(x[R0]), [x1] "v"(x[R0 + 1]),
+                     [x2] "v"(x[R0 + 2]), [x3] "v"(x[R0 + 3]), [c] "s"(c), [nm] "v"(nm));
+    }
+    // 2
+    asm volatile("v_mfma_f32_32x32x16_bf16 %[o], %[a], %[b], %[o]\n\t"
+                 FA_FMA("%[p4]", "%[x4]") FA_FMA("%[p5]", "%[x5]") FA_FMA("%[p6]", "%[x6]") FA_FMA("%[p7]", "%[x7]")
+                 : [o] "+a"(oacc[0][DB0]), [p4] "=&v"(p4), [p5] "=&v"(p5), [p6] "=&v"(p6), [p7] "=&v"(p7)
+                 : [a] "v"(o.v[0]), [b] "v"(b0), [x4] "v"(x[R0 + 4]), [x5] "v"(x[R0 + 5]),
+                   [x6] "v"(x[R0 + 6]), [x7] "v"(x[R0 + 7]), [c] "s"(c), [nm] "v"(nm));
+    // 3
+    if constexpr (S0 == 0) {
+      asm volatile("v_mfma_f32_32x32x16_bf16 %[s], %[a], %[b], 0\n\t"
+                   "v_exp_f32 %[p0], %[p0]\n\tv_exp_f32 %[p1], %[p1]\n\t"
+                   : [s] "=&v"(s_nxt[1]), [p0] "+v"(p0), [p1] "+v"(p1)
+                   : [a] "v"(o.k[0]), [b] "a"(qf[1][S0]));
+    } else {
+      asm volatile("v_mfma_f32_32x32x16_bf16 %[s], %[a], %[b], %[s]\n\t"
+                   "v_exp_f32 %[p0], %[p0]\n\tv_exp_f32 %[p1], %[p1]\n\t"
+                   : [s] "+v"(s_nxt[1]), [p0] "+v"(p0), [p1] "+v"(p1)
+                   : [a] "v"(o.k[0]), [b] "a"(qf[1][S0]));
+    }
+    // 4
+    asm volatile("v_mfma_f32_32x32x16_bf16 %[o], %[a], %[b], %[o]\n\t"
+                 "v_exp_f32 %[p2], %[p2]\n\tv_exp_f32 %[p3], %[p3]\n\t"
+                 : [o] "+a"(oacc[1][DB0]), [p2] "+v"(p2), [p3] "+v"(p3)
+                 : [a] "v"(o.v[0]), [b] "v"(b1));
+    // 5
+    asm volatile("v_mfma_f32_32x32x16_bf16 %[s], %[a], %[b], %[s]\n\t"
+                 "v_exp_f32 %[p4], %[p4]\n\tv_exp_f32 %[p5], %[p5]\n\t"
+                 "v_cvt_pk_bf16_f32 %[k0], %[p0], %[p1]\n\t"
+                 : [s] "+v"(s_nxt[0]), [p4] "+v"(p4), [p5] "+v"(p5), [k0] "=&v"(k0)
+                 : [a] "v"(o.k[1]), [b] "a"(qf[0][S0 + 1]), [p0] "v"(p0), [p1] "v"(p1));
+    // 6
+    asm volatile("v_mfma_f32_32x32x16_bf16 %[o], %[a], %[b], %[o]\n\t"
+                 "v_exp_f32 %[p6], %[p6]\n\tv_exp_f32 %[p7], %[p7]\n\t"
+                 "v_cvt_pk_bf16_f32 %[k1], %[p2], %[p3]\n\t"
+                 "v_add_f32 %[t0], %[p0], %[p1]\n\t"
+                 : [o] "+a"(oacc[0][DB0 + 1]), [p6] "+v"(p6), [p7] "+v"(p7), [k1] "=&v"(k1), [t0] "=&v"(t0)
+                 : [a] "v"(o.v[1]), [b] "v"(b0), [p0] "v"(p0), [p1] "v"(p1), [p2] "v"(p2), [p3] "v"(p3));
+    // 7
+    asm volatile("v_mfma_f32_32x32x16_bf16 %[s], %[a], %[b], %[s]\n\t"
+                 "v_cvt_pk_bf16_f32 %[k2], %[p4], %[p5]\n\t"
+                 "v_add_f32 %[t1], %[p2], %[p3]\n\t"
+                 "v_add_f32 %[t2], %[p4], %[p5]\n\t"
+                 : [s] "+v"(s_nxt[1]), [k2] "=&v"(k2), [t1] "=&v"(t1), [t2] "=&v"(t2)
+                 : [a] "v"(o.k[1]), [b] "a"(qf[1][S0 + 1]), [p2] "v"(p2), [p3] "v"(p3), [p4] "v"(p4),
+                   [p5] "v"(p5));
+    // 8
+    asm volatile("v_mfma_f32_32x32x16_bf16 %[o], %[a], %[b], %[o]\n\t"
+                 "v_cvt_pk_bf16_f32 %[k3], %[p6], %[p7]\n\t"
+                 "v_add_f32 %[t3], %[p6], %[p7]\n\t"
+                 "v_add_f32 %[t0], %[t0], %[t1]\n\t"
+                 "v_add_f32 %[t2], %[t2], %[t3]\n\t"
+                 "v_add_f32 %[t0], %[t0], %[t2]\n\t"
+                 "v_add_f32 %[l], %[l], %[t0]\n\t"
+                 : [o] "+a"(oacc[1][DB0 + 1]), [k3] "=&v"(k3), [t3] "=&v"(t3), [t0] "+v"(t0),
+                   [t2] "+v"(t2), [l] "+v"(lsum[RB])
+                 : [a] "v"(o.v[1]), [b] "v"(b1), [p6] "v"(p6), [p7] "v"(p7), [t1] "v"(t1));
+#undef FA_FMA
+    p_cur[RB][R0 / 2] = k0;
+    p_cur[RB][R0 / 2 + 1] = k1;
+    p_cur[RB][R0 / 2 + 2] = k2;
+    p_cur[RB][R0 / 2 + 3] = k3;
+    // The LDS reads of the next quarter go first in the quarter.
+    __builtin_amdgcn_sched_group_barrier(0x100, KQ + 2 * VQ, 0);
+  };
+
+  // Masking of block b after the fact: P is formed again from the scores
+  // with the keys past lim(rb) cleared (whatever a stale score produced is
+  // dropped), and so are the lane's P sums.
+  auto apply_mask = [&](int b, const f32x16 (&sacc)[2], uint32_t (&pk)[2][8], float (&lsum)[2]) {
+    consume(pk, lsum);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int room = mask_room(b, rb);
+      lsum[rb] = 0.f;
+      exp8(std::true_type{}, R0c{}, sacc[rb], m_ref[rb], room, pk[rb], lsum[rb]);
+      exp8(std::true_type{}, R8c{}, sacc[rb], m_ref[rb], room, pk[rb], lsum[rb]);
     }
   };
 
-  // The wave feeding the matrix core runs at raised issue priority, so the
-  // neighbouring wave's vector work fills the gaps instead of delaying it.
-  auto qk = [&](int j) {
-    __builtin_amdgcn_s_setprio(1);
-    const bf16* sk = sK + (j % kKBuf) * C::KTILE + col * C::KROW + half * 8;
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s)
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + kb * 32 * C::KROW + s * 16);
-        sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
-      }
-    pipeline_schedule(std::integral_constant<int, C::KS * C::NKB>{});
-    __builtin_amdgcn_s_setprio(0);
+  // One pipeline step around block b: four quarters, each using operands
+  // read during the one before; the last reads the first operands of the
+  // next step (K buffer NKB, V buffer NVB, half NHB).  Masking and the
+  // exact-maximum path follow the quarters as rare branches.
+  auto step = [&](auto kb, auto vb, auto hb, auto nkb, auto nvb, auto nhb, int b, Ops& ops,
+                  f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], uint32_t (&p_cur)[2][8],
+                  const uint32_t (&p_prv)[2][8]) {
+    using Q0 = std::integral_constant<int, 0>;
+    using Q1 = std::integral_constant<int, 1>;
+    using Q2 = std::integral_constant<int, 2>;
+    using Q3 = std::integral_constant<int, 3>;
+    float lsum[2] = {0.f, 0.f};
+    Ops n1 = load_ops(kb, vb, hb, Q1{});
+    quarter(Q0{}, ops, s_nxt, s_cur, p_cur, p_prv, lsum);
+    __builtin_amdgcn_sched_barrier(0);
+    Ops n2 = load_ops(kb, vb, hb, Q2{});
+    quarter(Q1{}, n1, s_nxt, s_cur, p_cur, p_prv, lsum);
+    __builtin_amdgcn_sched_barrier(0);
+    Ops n3 = load_ops(kb, vb, hb, Q3{});
+    quarter(Q2{}, n2, s_nxt, s_cur, p_cur, p_prv, lsum);
+    __builtin_amdgcn_sched_barrier(0);
+    ops = load_ops(nkb, nvb, nhb, Q0{});
+    quarter(Q3{}, n3, s_nxt, s_cur, p_cur, p_prv, lsum);
+    __builtin_amdgcn_sched_barrier(0);
+    if (needs_mask(b)) apply_mask(b, s_cur, p_cur, lsum);
+    fixup(b, s_cur, p_cur, lsum);
   };
 
-  auto pv = [&](int j) {
-    __builtin_amdgcn_s_setprio(1);
-    const bf16* sv = sV + (j % kVBuf) * C::VTILE + col * C::VROW + half * 8;
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 b = __builtin_bit_cast(
-            bf16x8, u32x4{pk[kb][4 * t], pk[kb][4 * t + 1], pk[kb][4 * t + 2], pk[kb][4 * t + 3]});
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sv + db * 32 * C::VROW + (2 * kb + t) * 16);
-          oacc[db] = mfma_32x32x16(a, b, oacc[db]);
-        }
-      }
-    pipeline_schedule(std::integral_constant<int, C::NKB * 2 * C::NDB>{});
-    __builtin_amdgcn_s_setprio(0);
-  };
-
-  // Masks keys past the end and, on diagonal tiles, keys after the query;
-  // then P = 2^(s*c - m) against the current reference m, the row sum and
-  // the bf16 pairs of P.  The reference only has to keep every P small, so
-  // instead of a row maximum per tile the tile's own sum decides: if any
-  // lane's share exceeds 2^tau (or is not finite: m = -inf before the first
-  // visible key), the wave takes the exact path once — row maximum, new
-  // reference, O and l rescaled, P recomputed.  Either way every P <= 2^tau.
-  auto exp_tile = [&](float m_use, float& lsum) {
-    lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2_hw(__builtin_fmaf(sacc[kb][r], c, -m_use));
-        const float p1 = exp2_hw(__builtin_fmaf(sacc[kb][r + 1], c, -m_use));
-        lsum += p0 + p1;
-        pk[kb][r >> 1] = pack_bf16x2(p0, p1);
-      }
-  };
-  auto softmax = [&](int j) {
-    const int k0 = j * BC;
-    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wq0 + off);
-    if (need_mask) {
-      const int lim = CAUSAL ? min(Nk - 1, qi + off) : Nk - 1;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > lim) sacc[kb][r] = kNegInf;
-        }
+  // Tile iteration j (buffer U = j % kNBuf) first requests K tile j+4 and V
+  // tile j+3 (into the buffers of K tile j and V tile j-1, whose last readers
+  // passed the previous barrier), then runs the steps around blocks 2j+1 and
+  // 2j+2, which read K tile j+1 and V tile j (and, ahead, the first
+  // operands of K tile j+2 and V tile j+1), and finally waits for all but
+  // its own requests, so K tile j+3 and V tile j+2 are in place for
+  // iteration j+1.
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
+  Ops ops;
+  auto iteration = [&](auto u, int j) {
+    constexpr int U = decltype(u)::value;
+    using KB = std::integral_constant<int, (U + 1) % kNBuf>;
+    using VB = std::integral_constant<int, U>;
+    using NKB = std::integral_constant<int, (U + 2) % kNBuf>;
+    using NVB = std::integral_constant<int, (U + 1) % kNBuf>;
+    const bool more_k = j + 4 < n_tiles, more_v = j + 3 < n_tiles;
+    if (more_k) issue_k(std::integral_constant<int, U>{}, j + 4);
+    if (more_v) issue_v(std::integral_constant<int, (U + 3) % kNBuf>{}, j + 3);
+    if (j < njw) {
+      step(KB{}, VB{}, H0{}, KB{}, VB{}, H1{}, 2 * j + 1, ops, sB, sA, pB, pA);
+      step(KB{}, VB{}, H1{}, NKB{}, NVB{}, H0{}, 2 * j + 2, ops, sA, sB, pA, pB);
     }
-    float lsum;
-    exp_tile(m_ref, lsum);  // m_ref = -inf gives +inf/NaN sums, caught below
-    if (wave_any(!(lsum <= kSumBound))) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = max_across_halves(mx);
-      const float m_new = fmaxf(m_ref, mx * c);  // c > 0, so -inf stays -inf
-      if (m_new != m_ref) {
-        const float alpha = exp2_hw(m_ref - m_new);  // 0 when m_ref was -inf
-        l_part *= alpha;
-#pragma unroll
-        for (int i = 0; i < C::NDB; ++i) oacc[i] *= alpha;
-        m_ref = m_new;
-      }
-      exp_tile(m_ref == kNegInf ? 0.f : m_ref, lsum);
+    if (more_k) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::IPW));
+    } else if (more_v) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::IPW));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    l_part += lsum;
+    __syncthreads();
   };
 
   // ------------------------------------------------------------- main loop
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
   if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (n_tiles > 1) load_tile(1);
-  }
-  __syncthreads();
-
-  // Group B finishes the previous tile's P V first, so it runs one extra
-  // iteration after the last tile.
-  for (int j = 0; j <= n_tiles; ++j) {
-    if (!group_b) {
-      if (j < nt_w) {
-        qk(j);
-        softmax(j);
-        pv(j);
-      }
-    } else {
-      if (j >= 1 && j - 1 < nt_w) pv(j - 1);
-      if (j < nt_w) {
-        qk(j);
-        softmax(j);
-      }
+    // K tiles 0-2 and V tiles 0-1 before the first barrier; K tile 3 and V
+    // tile 2 (the requests of "iteration -1") after it.
+    issue_k(B0{}, 0);
+    issue_v(B0{}, 0);
+    if (n_tiles > 1) {
+      issue_k(B1{}, 1);
+      issue_v(B1{}, 1);
     }
-    // Stage tile j+1 (loaded one iteration ago) and fetch tile j+2.
-    if (j + 1 < n_tiles) store_tile(j + 1);
-    if (j + 2 < n_tiles) load_tile(j + 2);
+    if (n_tiles > 2) issue_k(B2{}, 2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
+    if (n_tiles > 3) issue_k(B3{}, 3);
+    if (n_tiles > 2) issue_v(B2{}, 2);
+    if (nbw > 0) {  // block 0 and the scores of block 1 before the first tile iteration
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        f32x16(&sacc)[2] = hb ? sB : sA;
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+          const bf16x8 a = *reinterpret_cast<const lds_bf16x8*>(lds + k_off[s] + hb * 32 * ROWB);
+          if (s == 0) {
+            qk_first(sacc[0], a, qf[0][s]);
+            qk_first(sacc[1], a, qf[1][s]);
+          } else {
+            qk_next(sacc[0], a, qf[0][s]);
+            qk_next(sacc[1], a, qf[1][s]);
+          }
+        }
+      }
+      products_done();
+      float lsum[2] = {0.f, 0.f};
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int room = mask_room(0, rb);
+        exp8(std::true_type{}, R0c{}, sA[rb], m_ref[rb], room, pA[rb], lsum[rb]);
+        exp8(std::true_type{}, R8c{}, sA[rb], m_ref[rb], room, pA[rb], lsum[rb]);
+      }
+      fixup(0, sA, pA, lsum);
+      ops = load_ops(B1{}, B0{}, H0{}, std::integral_constant<int, 0>{});
+    }
+    for (int j = 0; j < n_tiles; j += kNBuf) {
+      iteration(B0{}, j);
+      if (j + 1 >= n_tiles) break;
+      iteration(B1{}, j + 1);
+      if (j + 2 >= n_tiles) break;
+      iteration(B2{}, j + 2);
+      if (j + 3 >= n_tiles) break;
+      iteration(B3{}, j + 3);
+    }
   }
+
+  products_done();  // the epilogue reads O
 
   // Epilogue: one division per row, O in bf16, LSE = ln2 * (m + log2 l).
-  const float l_tot = sum_across_halves(l_part);
-  if (qi < Nq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16* orow = O + qbase + (size_t)qi * D;
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = qi0 + 32 * rb;
+    const float l_tot = sum_across_halves(l_part[rb]);
+    if (row < Nq) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      bf16* orow = O + qbase + (size_t)row * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                         pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * half) = w;
-      }
-    if (half == 0)
-      LSE[(size_t)bh * Nq + qi] = l_tot > 0.f ? (m_ref + log2_hw(l_tot)) * kLn2 : kNegInf;
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 w = {pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv),
+                           pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * half) = w;
+        }
+      if (half == 0)
+        LSE[(size_t)bh * Nq + row] = l_tot > 0.f ? (m_ref[rb] + log2_hw(l_tot)) * kLn2 : kNegInf;
+    }
   }
 }
 
@@ -350,16 +679,13 @@ template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a) {
   const int n_qtiles = (a.Nq + kBR - 1) / kBR;
   const int BH = a.B * a.H;
-  // c > 0 keeps masked scores (-inf) at -inf after scaling.  A zero scale
-  // becomes 1e-30: every product with a finite score then rounds away
-  // against the reference, so the weights are exactly uniform, as for 0.
-  const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
-  const int neg = a.scale < 0.f ? 1 : 0;
+  // Scores enter the exponent as s * c (log2 units); masking acts on P,
+  // so c may have either sign or be zero.
+  const float c = a.scale * kLog2e;
   const dim3 grid((unsigned)(n_qtiles * BH));
   const dim3 block(kThreads);
   void* args[] = {(void*)&a.q, (void*)&a.k, (void*)&a.v, (void*)&a.o, (void*)&a.lse,
-                  (void*)&BH, (void*)&a.Nq, (void*)&a.Nk, (void*)&c, (void*)&neg,
-                  (void*)&n_qtiles};
+                  (void*)&BH, (void*)&a.Nq, (void*)&a.Nk, (void*)&c, (void*)&n_qtiles};
   return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL>), grid, block,
                          args, 0, a.stream);
 }
@@ -368,7 +694,7 @@ hipError_t launch(const FwdArgs& a) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
   if (a.d == 128) return a.causal ? launch<128, true>(a) : launch<128, false>(a);
-  return a.causal ? launch<64, true>(a) : launch<64, false>(a);
+  return launch_fwd_bf16_d64(a);
 }
 
 long long fwd_bf16_grid(int B, int H, int Nq) {

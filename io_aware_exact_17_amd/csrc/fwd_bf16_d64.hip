@@ -1,0 +1,376 @@
+// fwd_bf16_d64.hip — tiled exact-attention forward pass, bf16 in / bf16 out,
+// head dimension 64, for gfx950.  (Head dimension 128 runs the kernel in
+// fwd_bf16.hip: at d=64 the softmax outweighs the matrix work per score, and
+// two waves per SIMD in opposite phase hide it better than one wave that
+// pipelines both.)
+//
+// Method (FlashAttention explainer, cztcode.com/2026/5368, §2-§3; Flash
+// Attention wiki note, astro-wiki, "Online Softmax", "Tiling" and the
+// FlashAttention-2 notes): a workgroup owns a tile of query rows and streams
+// the key/value tiles past it (query tile outer, key tile inner).  Each query
+// row keeps a running maximum m, a running sum l of exp(s - m) and an
+// unnormalised output u; when m grows, l and u are rescaled by exp(m_old -
+// m_new); the division u / l happens once, after the last key tile.  Score and
+// probability tiles live only in registers.  Key tiles wholly above the
+// causal diagonal are never loaded (explainer §6).
+//
+// Mapping to CDNA4:
+//  * 8 waves x 32 query rows = 256 rows per workgroup, one workgroup per CU,
+//    two waves per SIMD.  Both products run on the matrix cores as
+//    v_mfma_f32_32x32x16_bf16.
+//  * The score tile is formed transposed, S^T = K Q^T, so every lane holds
+//    one query column: row max and row sum are in-lane reductions plus one
+//    exchange between lane halves (v_permlane32_swap); no reduction crosses
+//    waves.  The S^T accumulators, rounded to bf16, are directly the B operand
+//    of O^T += V^T P^T, so P never leaves registers.
+//  * Two wave groups in opposite phase.  Waves 0-3 (group A) handle each key
+//    tile as  S = K Q^T -> softmax -> O += P V;  waves 4-7 (group B, one on
+//    each SIMD next to a group-A wave) as  O += P V of the previous tile ->
+//    S = K Q^T -> softmax.  After each barrier the two waves sharing a SIMD
+//    therefore run their vector-ALU softmax while the other one feeds the
+//    matrix core, instead of both waiting on the same unit.
+//  * K tiles are staged row-major in LDS; V tiles transposed (V^T, keys
+//    contiguous) with the key order permuted inside each group of 16 so that
+//    one 16-byte LDS read yields exactly the 8 keys a lane's P registers hold.
+//    Row strides are padded by 16 bytes (no bank conflicts).  Two K buffers
+//    and three V^T buffers (group B reads the previous V tile); one barrier
+//    per tile.  The tile after the next is fetched from HBM into registers
+//    with 16-byte loads a whole tile ahead: waves 0-3 move V tiles
+//    (transposing them in registers), waves 4-7 move K tiles.
+//  * exp is 2^x on v_exp_f32 with log2(e) folded into the scale.  The
+//    reference maximum is not recomputed per tile: P is formed against the
+//    current reference and only when a tile's P sum exceeds 2^8 (so some P
+//    could exceed 256 before rounding to bf16) is the exact row maximum
+//    taken, the reference moved and the output accumulator rescaled.  That
+//    happens on the first tile and rarely afterwards; the mathematics is
+//    unchanged because the final division uses the same reference.
+//  * Workgroups are issued heaviest query tile first; consecutive workgroup
+//    ids walk the heads, so when B*H is a multiple of 8 every tile of a head
+//    lands on the same XCD (workgroups are dealt round-robin to the 8 XCDs)
+//    and shares its K/V in that XCD's L2.
+#include "cdna4.hpp"
+#include "kernels.hpp"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kMovers = 256;      // threads staging each operand
+constexpr int kBR = 256;          // query rows per workgroup (8 waves x 32)
+constexpr int kKBuf = 2;          // LDS K buffers
+constexpr int kVBuf = 3;          // LDS V^T buffers
+constexpr float kSumBound = 256.f;  // a tile's P sum per lane half stays <= 2^8
+constexpr int kPrefetch = 6;      // LDS operand reads kept ahead of the matrix cores
+
+template <int D>
+struct FwdCfg {
+  static constexpr int BC = 8192 / D;    // keys per tile: 64 for d=128, 128 for d=64
+  static constexpr int KS = D / 16;      // k-steps of S^T = K Q^T
+  static constexpr int NKB = BC / 32;    // 32-key blocks per tile
+  static constexpr int NDB = D / 32;     // 32-row blocks of O^T
+  static constexpr int KROW = D + 8;     // LDS row stride of K (elements)
+  static constexpr int VROW = BC + 8;    // LDS row stride of V^T (elements)
+  static constexpr int KTILE = BC * KROW;
+  static constexpr int VTILE = D * VROW;
+  static constexpr int KCHUNKS = BC * D / 8 / kMovers;   // 16-byte K chunks per K mover
+  static constexpr int VBLOCKS = (BC / 4) * (D / 8);     // 4-key x 8-dim V blocks per tile
+  static constexpr int LDS_ELEMS = kKBuf * KTILE + kVBuf * VTILE;
+  static_assert(KCHUNKS == 4 && KCHUNKS * kMovers * 8 == BC * D, "K tile split");
+  static_assert(VBLOCKS == kMovers, "one V block per V mover");
+};
+
+// Position of a group of four keys inside its group of 16 in the V^T layout:
+// the two middle groups are swapped, so positions 8h..8h+7 hold keys
+// {4h..4h+3, 8+4h..8+4h+3} — the keys accumulator registers 0..7 of lane
+// half h cover in the S^T layout.
+__device__ __forceinline__ int vt_pos4(int group4) {
+  return ((group4 & 1) << 1) | ((group4 >> 1) & 1);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int Nq, int Nk,
+    float c, int negate_q, int n_qtiles) {
+  using C = FwdCfg<D>;
+  constexpr int BC = C::BC;
+  __shared__ __attribute__((aligned(16))) bf16 smem[C::LDS_ELEMS];
+  bf16* const sK = smem;                      // kKBuf K tiles
+  bf16* const sV = smem + kKBuf * C::KTILE;   // kVBuf V^T tiles
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool group_b = wave >= 4;
+  const int col = lane & 31;   // query column of this lane in S^T / O^T
+  const int half = lane >> 5;  // which 8-wide k slice / 4-row group this lane holds
+
+  // Heaviest query tile first; heads vary fastest.
+  const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
+  const int bh = (int)(blockIdx.x % BH);
+  const int q0 = qt * kBR;
+  const int off = Nk - Nq;  // bottom-right causal alignment
+  const size_t qbase = (size_t)bh * Nq * D;
+  const size_t kbase = (size_t)bh * Nk * D;
+
+  const int kv_end = CAUSAL ? min(Nk, q0 + kBR + off) : Nk;
+  const int n_tiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+
+  const int wq0 = q0 + wave * 32;  // first query row of this wave
+  const int qi = wq0 + col;        // this lane's query row
+  const int kv_end_w = CAUSAL ? min(Nk, wq0 + 32 + off) : Nk;
+  const int nt_w = kv_end_w > 0 ? (kv_end_w + BC - 1) / BC : 0;  // tiles this wave needs
+
+  // Q^T operand: lane holds Q[qi][16s + 8*half + 0..7].  Rows past Nq read
+  // row Nq-1 (their results are never stored).
+  bf16x8 qf[C::KS];
+  {
+    const uint32_t flip = negate_q ? 0x80008000u : 0u;  // exact sign flip for a negative scale
+    const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)min(qi, Nq - 1) * D);
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      u32x4 w = src[2 * s + half];
+      w ^= flip;
+      qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  // ---------------------------------------------------------- tile staging
+  // Waves 0-3 move V, waves 4-7 move K, four 16-byte chunks per thread.
+  //   K mover mt: chunks mt + 256 i of the row-major tile, i.e. key
+  //     mt / (D/8) + (256 / (D/8)) i, 8 dims at (mt % (D/8)) * 8.
+  //   V mover mt: keys 4*vkg .. 4*vkg+3 of dims vdb*8 .. vdb*8+7, written to
+  //     V^T transposed.
+  const bool k_mover = tid >= kMovers;
+  const int mt = tid & (kMovers - 1);
+  constexpr int kKeysPerPass = kMovers / (D / 8);
+  const int vkg = mt % (BC / 4);
+  const int vdb = mt / (BC / 4);
+  const int first_key = k_mover ? mt / (D / 8) : 4 * vkg;
+  const int key_step = k_mover ? kKeysPerPass : 1;
+  const int dcol = k_mover ? (mt % (D / 8)) * 8 : vdb * 8;
+  u32x4 stg[4];
+
+  // The tile base is uniform, so loads take an SGPR base plus a 32-bit lane
+  // byte offset.  Keys past Nk read row Nk-1 instead: finite values whose
+  // scores are masked to -inf, so they carry zero weight.
+  auto load_tile = [&](int j) {
+    const int k0 = j * BC;
+    const char* base = reinterpret_cast<const char*>((k_mover ? K : V) + kbase + (size_t)k0 * D);
+    const int last = Nk - 1 - k0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(first_key + key_step * i, last);
+      stg[i] = *reinterpret_cast<const u32x4*>(base + (uint32_t)((key * D + dcol) * 2));
+    }
+  };
+  auto store_tile = [&](int j) {
+    if (k_mover) {
+      bf16* sk = sK + (j % kKBuf) * C::KTILE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(sk + (first_key + key_step * i) * C::KROW + dcol) = stg[i];
+    } else {
+      bf16* sv = sV + (j % kVBuf) * C::VTILE;
+      // 4 keys x 8 dims -> 8 rows of V^T, 4 keys each.
+      const int pos = 16 * (vkg >> 2) + 4 * vt_pos4(vkg & 3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t e01 = __builtin_amdgcn_perm(stg[1][i], stg[0][i], 0x05040100u);
+        const uint32_t e23 = __builtin_amdgcn_perm(stg[3][i], stg[2][i], 0x05040100u);
+        const uint32_t o01 = __builtin_amdgcn_perm(stg[1][i], stg[0][i], 0x07060302u);
+        const uint32_t o23 = __builtin_amdgcn_perm(stg[3][i], stg[2][i], 0x07060302u);
+        *reinterpret_cast<u32x2*>(sv + (vdb * 8 + 2 * i) * C::VROW + pos) = u32x2{e01, e23};
+        *reinterpret_cast<u32x2*>(sv + (vdb * 8 + 2 * i + 1) * C::VROW + pos) = u32x2{o01, o23};
+      }
+    }
+  };
+
+  // ------------------------------------------------------ per-tile stages
+  f32x16 oacc[C::NDB];
+#pragma unroll
+  for (int i = 0; i < C::NDB; ++i) oacc[i] = f32x16{};
+  float m_ref = kNegInf;  // reference maximum, log2 units (score * c)
+  float l_part = 0.f;     // this lane half's share of the row sum
+  f32x16 sacc[C::NKB];
+  uint32_t pk[C::NKB][8];  // bf16 P pairs of the latest softmax
+
+  // Matrix-core loops keep kPrefetch LDS operand reads in flight: the
+  // schedule is pinned to  kPrefetch reads, then (1 MFMA, 1 read) pairs,
+  // then the remaining MFMAs, so no MFMA waits on a read issued just before.
+  auto pipeline_schedule = [&](auto n_mfma) {
+    constexpr int N = decltype(n_mfma)::value;
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kPrefetch < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // The wave feeding the matrix core runs at raised issue priority, so the
+  // neighbouring wave's vector work fills the gaps instead of delaying it.
+  auto qk = [&](int j) {
+    __builtin_amdgcn_s_setprio(1);
+    const bf16* sk = sK + (j % kKBuf) * C::KTILE + col * C::KROW + half * 8;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + kb * 32 * C::KROW + s * 16);
+        sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
+      }
+    pipeline_schedule(std::integral_constant<int, C::KS * C::NKB>{});
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto pv = [&](int j) {
+    __builtin_amdgcn_s_setprio(1);
+    const bf16* sv = sV + (j % kVBuf) * C::VTILE + col * C::VROW + half * 8;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, u32x4{pk[kb][4 * t], pk[kb][4 * t + 1], pk[kb][4 * t + 2], pk[kb][4 * t + 3]});
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sv + db * 32 * C::VROW + (2 * kb + t) * 16);
+          oacc[db] = mfma_32x32x16(a, b, oacc[db]);
+        }
+      }
+    pipeline_schedule(std::integral_constant<int, C::NKB * 2 * C::NDB>{});
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Masks keys past the end and, on diagonal tiles, keys after the query;
+  // then P = 2^(s*c - m) against the current reference m, the row sum and
+  // the bf16 pairs of P.  The reference only has to keep every P small, so
+  // instead of a row maximum per tile the tile's own sum decides: if any
+  // lane's share exceeds 2^tau (or is not finite: m = -inf before the first
+  // visible key), the wave takes the exact path once — row maximum, new
+  // reference, O and l rescaled, P recomputed.  Either way every P <= 2^tau.
+  auto exp_tile = [&](float m_use, float& lsum) {
+    lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = exp2_hw(__builtin_fmaf(sacc[kb][r], c, -m_use));
+        const float p1 = exp2_hw(__builtin_fmaf(sacc[kb][r + 1], c, -m_use));
+        lsum += p0 + p1;
+        pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+      }
+  };
+  auto softmax = [&](int j) {
+    const int k0 = j * BC;
+    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wq0 + off);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(Nk - 1, qi + off) : Nk - 1;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key > lim) sacc[kb][r] = kNegInf;
+        }
+    }
+    float lsum;
+    exp_tile(m_ref, lsum);  // m_ref = -inf gives +inf/NaN sums, caught below
+    if (wave_any(!(lsum <= kSumBound))) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = max_across_halves(mx);
+      const float m_new = fmaxf(m_ref, mx * c);  // c > 0, so -inf stays -inf
+      if (m_new != m_ref) {
+        const float alpha = exp2_hw(m_ref - m_new);  // 0 when m_ref was -inf
+        l_part *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::NDB; ++i) oacc[i] *= alpha;
+        m_ref = m_new;
+      }
+      exp_tile(m_ref == kNegInf ? 0.f : m_ref, lsum);
+    }
+    l_part += lsum;
+  };
+
+  // ------------------------------------------------------------- main loop
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (n_tiles > 1) load_tile(1);
+  }
+  __syncthreads();
+
+  // Group B finishes the previous tile's P V first, so it runs one extra
+  // iteration after the last tile.
+  for (int j = 0; j <= n_tiles; ++j) {
+    if (!group_b) {
+      if (j < nt_w) {
+        qk(j);
+        softmax(j);
+        pv(j);
+      }
+    } else {
+      if (j >= 1 && j - 1 < nt_w) pv(j - 1);
+      if (j < nt_w) {
+        qk(j);
+        softmax(j);
+      }
+    }
+    // Stage tile j+1 (loaded one iteration ago) and fetch tile j+2.
+    if (j + 1 < n_tiles) store_tile(j + 1);
+    if (j + 2 < n_tiles) load_tile(j + 2);
+    __syncthreads();
+  }
+
+  // Epilogue: one division per row, O in bf16, LSE = ln2 * (m + log2 l).
+  const float l_tot = sum_across_halves(l_part);
+  if (qi < Nq) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16* orow = O + qbase + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                         pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * half) = w;
+      }
+    if (half == 0)
+      LSE[(size_t)bh * Nq + qi] = l_tot > 0.f ? (m_ref + log2_hw(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const FwdArgs& a) {
+  const int n_qtiles = (a.Nq + kBR - 1) / kBR;
+  const int BH = a.B * a.H;
+  // c > 0 keeps masked scores (-inf) at -inf after scaling.  A zero scale
+  // becomes 1e-30: every product with a finite score then rounds away
+  // against the reference, so the weights are exactly uniform, as for 0.
+  const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+  const int neg = a.scale < 0.f ? 1 : 0;
+  const dim3 grid((unsigned)(n_qtiles * BH));
+  const dim3 block(kThreads);
+  void* args[] = {(void*)&a.q, (void*)&a.k, (void*)&a.v, (void*)&a.o, (void*)&a.lse,
+                  (void*)&BH, (void*)&a.Nq, (void*)&a.Nk, (void*)&c, (void*)&neg,
+                  (void*)&n_qtiles};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL>), grid, block,
+                         args, 0, a.stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16_d64(const FwdArgs& a) {
+  return a.causal ? launch<64, true>(a) : launch<64, false>(a);
+}
+
+}  // namespace fa

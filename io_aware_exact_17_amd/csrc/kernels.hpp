@@ -36,7 +36,8 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
-hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_bf16(const FwdArgs& a);      // d = 128 here, d = 64 below
+hipError_t launch_fwd_bf16_d64(const FwdArgs& a);  // fwd_bf16_d64.hip
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 
