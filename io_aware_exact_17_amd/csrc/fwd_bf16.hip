@@ -65,6 +65,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -257,7 +259,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const uint32_t lds_wave = (uint32_t)(size_t)lds + wave * C::IPW * 1024;
   auto issue = [&](const char* base, int region, int j) {
     const char* t = base + (size_t)j * TB;
-    const uint32_t dst = lds_wave + region;
+    uint32_t dst = lds_wave;
+    asm volatile("" : "+s"(dst));
+    dst += region;
     if ((j + 1) * kBC <= Nk) {
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i) copy_to_lds(t, g_off[i], dst + i * 1024);
@@ -380,7 +384,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // visible keys, moved reference, l and O rescaled (O then holds the P V of
   // the blocks before b), P recomputed.  Every P then stays <= 2^8.
   auto fixup = [&](int b, const f32x16 (&sacc)[2], uint32_t (&pk)[2][8], float (&lsum)[2]) {
-    if (wave_any(!(lsum[0] <= kSumBound) || !(lsum[1] <= kSumBound))) {
+    if (__builtin_expect(wave_any(!(lsum[0] <= kSumBound) || !(lsum[1] <= kSumBound)), 0)) {
+      [[unlikely]];
       consume(pk, lsum);
       products_done();  // O is read below
       const bool masked = needs_mask(b);
@@ -395,8 +400,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         const float m_new = fmaxf(m_ref[rb], mx);
         const float alpha = m_new != m_ref[rb] ? exp2_hw(m_ref[rb] - m_new) : 1.f;  // 0 from -inf
         l_part[rb] *= alpha;
+        // O is rescaled one register at a time in place (read, multiply,
+        // write back through a single temporary): written as a plain vector
+        // product the compiler stages all of O in vector registers, and the
+        // room that takes is then missing from the whole loop.
 #pragma unroll
-        for (int i = 0; i < C::NDB; ++i) oacc[rb][i] *= alpha;
+        for (int i = 0; i < C::NDB; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float x = oacc[rb][i][e];
+            float t;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(x), "=&v"(t)
+                         : "v"(alpha));
+            oacc[rb][i][e] = x;
+          }
         // The next products into O are inline assembly the compiler does not
         // see: give the rescaled accumulators their wait states here.
         asm volatile("s_nop 7" ::: "memory");
@@ -557,7 +575,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     ops = load_ops(nkb, nvb, nhb, Q0{});
     quarter(Q3{}, n3, s_nxt, s_cur, p_cur, p_prv, lsum);
     __builtin_amdgcn_sched_barrier(0);
-    if (needs_mask(b)) apply_mask(b, s_cur, p_cur, lsum);
+    if (__builtin_expect(needs_mask(b), 0)) {
+      [[unlikely]];
+      apply_mask(b, s_cur, p_cur, lsum);
+    }
     fixup(b, s_cur, p_cur, lsum);
   };
 
@@ -600,8 +621,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   using B2 = std::integral_constant<int, 2>;
   using B3 = std::integral_constant<int, 3>;
   if (n_tiles > 0) {
-    // K tiles 0-2 and V tiles 0-1 before the first barrier; K tile 3 and V
-    // tile 2 (the requests of "iteration -1") after it.
+    // Requests in order: Q (above), K tile 0, V tile 0, K tile 1, V tile 1,
+    // K tile 2.  The block-0 scores need only Q and K tile 0, so the first
+    // barrier waits for those; K tile 3 and V tile 2 (the requests of
+    // "iteration -1") follow it.  The second barrier waits for the rest of
+    // the first five tiles and keeps the first tile iteration's request into
+    // K buffer 0 behind every wave's reads of K tile 0.
     issue_k(B0{}, 0);
     issue_v(B0{}, 0);
     if (n_tiles > 1) {
@@ -609,7 +634,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       issue_v(B1{}, 1);
     }
     if (n_tiles > 2) issue_k(B2{}, 2);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (n_tiles > 2) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * C::IPW));
+    } else if (n_tiles > 1) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * C::IPW));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::IPW));
+    }
     __syncthreads();
     if (n_tiles > 3) issue_k(B3{}, 3);
     if (n_tiles > 2) issue_v(B2{}, 2);
@@ -630,16 +661,30 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         }
       }
       products_done();
-      float lsum[2] = {0.f, 0.f};
+      // Block 0 sets the reference: its exact row maximum over the visible
+      // keys (O and l are still zero, so nothing is rescaled).
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const int room = mask_room(0, rb);
-        exp8(std::true_type{}, R0c{}, sA[rb], m_ref[rb], room, pA[rb], lsum[rb]);
-        exp8(std::true_type{}, R8c{}, sA[rb], m_ref[rb], room, pA[rb], lsum[rb]);
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          mx = (8 * (r >> 2) + (r & 3) > room) ? mx : fmaxf(mx, sA[rb][r] * c);
+        m_ref[rb] = max_across_halves(mx);
+        const float m_use = m_ref[rb] == kNegInf ? 0.f : m_ref[rb];
+        exp8(std::true_type{}, R0c{}, sA[rb], m_use, room, pA[rb], l_part[rb]);
+        exp8(std::true_type{}, R8c{}, sA[rb], m_use, room, pA[rb], l_part[rb]);
       }
-      fixup(0, sA, pA, lsum);
-      ops = load_ops(B1{}, B0{}, H0{}, std::integral_constant<int, 0>{});
     }
+    if (n_tiles > 3) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::IPW));
+    } else if (n_tiles > 2) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::IPW));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __syncthreads();
+    if (nbw > 0) ops = load_ops(B1{}, B0{}, H0{}, std::integral_constant<int, 0>{});
     for (int j = 0; j < n_tiles; j += kNBuf) {
       iteration(B0{}, j);
       if (j + 1 >= n_tiles) break;
@@ -654,24 +699,39 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   products_done();  // the epilogue reads O
 
   // Epilogue: one division per row, O in bf16, LSE = ln2 * (m + log2 l).
+  // O leaves through LDS (free after the last barrier): each wave writes its
+  // 64 x D tile row-major into its own 16 KB region, with the 16-byte chunks
+  // of row r at slots c ^ (r % 16), then reads whole rows back and stores
+  // them with 16-byte writes, 1 KB contiguous per wave instruction.
+  lds_char* const otile = lds + wave * 64 * ROWB;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const int row = qi0 + 32 * rb;
+    const int r = 32 * rb + col;  // row within the wave's tile
     const float l_tot = sum_across_halves(l_part[rb]);
-    if (row < Nq) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      bf16* orow = O + qbase + (size_t)row * D;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
+    for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2 w = {pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv),
-                           pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * half) = w;
-        }
-      if (half == 0)
-        LSE[(size_t)bh * Nq + row] = l_tot > 0.f ? (m_ref[rb] + log2_hw(l_tot)) * kLn2 : kNegInf;
-    }
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 w = {pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv),
+                         pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv)};
+        const int chunk = 4 * db + g;  // dims 32db + 8g .. +7; this lane half holds +4h .. +4h+3
+        *reinterpret_cast<lds_u32x2*>(otile + r * ROWB + ((chunk ^ (r & 15)) * 16) + 8 * half) = w;
+      }
+    const int row = qi0 + 32 * rb;
+    if (half == 0 && row < Nq)
+      LSE[(size_t)bh * Nq + row] = l_tot > 0.f ? (m_ref[rb] + log2_hw(l_tot)) * kLn2 : kNegInf;
+  }
+  // Same wave wrote the region, so program order is enough between the
+  // writes and these reads.
+  constexpr int kRowsPerStore = 64 * 16 / ROWB;  // rows covered by 64 lanes x 16 B
+#pragma unroll
+  for (int it = 0; it < 64 / kRowsPerStore; ++it) {
+    const int r = it * kRowsPerStore + lane / C::CPR;
+    const int c = lane % C::CPR;
+    const u32x4 w = *reinterpret_cast<const lds_u32x4*>(otile + r * ROWB + ((c ^ (r & 15)) * 16));
+    const int row = wq0 + r;
+    if (row < Nq) *reinterpret_cast<u32x4*>(O + qbase + (size_t)row * D + c * 8) = w;
   }
 }
 

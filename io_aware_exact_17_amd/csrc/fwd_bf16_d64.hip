@@ -269,7 +269,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   auto softmax = [&](int j) {
     const int k0 = j * BC;
     const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wq0 + off);
-    if (need_mask) {
+    if (__builtin_expect(need_mask, 0)) {
+      [[unlikely]];
       const int lim = CAUSAL ? min(Nk - 1, qi + off) : Nk - 1;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
@@ -281,7 +282,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
     float lsum;
     exp_tile(m_ref, lsum);  // m_ref = -inf gives +inf/NaN sums, caught below
-    if (wave_any(!(lsum <= kSumBound))) {
+    if (__builtin_expect(wave_any(!(lsum <= kSumBound)), 0)) {
+      [[unlikely]];
       float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
