@@ -13,7 +13,8 @@ from HBM.  Every call is bracketed by HIP events on the stream it runs on.
 
 Prints one JSON line: `value` is the prefill rate in TFLOP/s (4*B*H*N^2*d/2
 algorithmic FLOPs over the prefill kernel's event time); the decode KV-read
-rates (GB/s) ride along in `decode`; `roofline` describes the prefill kernel
+rates (GB/s) ride along in `decode`, beside the read rate a plain streaming
+read kernel reaches on the same byte counts (the empirical ceiling); `roofline` describes the prefill kernel
 against the bf16 dense matrix-core peak; `cpu_baseline` times the fp64 oracle
 on a bounded sample of the prefill on the host.
 """
@@ -84,6 +85,32 @@ def cpu_baseline(budget_s: float):
             "kind": "oracle",
             "sample": f"{heads} of {s.H} heads of the causal N=8192 d=128 prefill, whole heads, "
                       f"fp64 NumPy with S and P materialised; {t_total:.1f} s"}
+
+
+def read_ceiling(torch, fa, dev, stream, small_bytes):
+    """Empirical read bandwidth (GB/s) of a plain streaming-read kernel
+    (fa_probe_read) for the single decode's byte count and for 8 GiB, each
+    repetition on a region no earlier repetition touched (cold, clean cache)."""
+    big = torch.empty(8 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(nbytes, offsets, skip):
+        ts = []
+        for i, off in enumerate(offsets):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fa.fa_probe_read(big[off:off + nbytes], sink=sink, stream=stream)
+            e1.record(stream)
+            e1.synchronize()
+            if i >= skip:
+                ts.append(e0.elapsed_time(e1))
+        return nbytes / (statistics.mean(ts) * 1e-3) / 1e9
+
+    small = timed(small_bytes, [i * small_bytes for i in range(12)], 2)
+    full = timed(big.numel(), [0, 0, 0], 1)
+    del big
+    return small, full
 
 
 def main():
@@ -177,6 +204,8 @@ def main():
     db_gbps = db_bytes / (statistics.mean(t_db) * 1e-3) / 1e9
     ds_gbps = ds_bytes / (statistics.mean(t_ds) * 1e-3) / 1e9
 
+    ceil_small, ceil_big = read_ceiling(torch, fa, dev, stream, ds_bytes)
+
     cpu = cpu_baseline(args.cpu_budget)
 
     line = {
@@ -210,7 +239,11 @@ def main():
                    "batched_kv_read": round(db_gbps, 1),
                    "single_kv_read": round(ds_gbps, 1),
                    "frac_of_hbm_peak": {"batched": round(db_gbps / PEAK_HBM_GBPS, 4),
-                                        "single": round(ds_gbps / PEAK_HBM_GBPS, 4)}},
+                                        "single": round(ds_gbps / PEAK_HBM_GBPS, 4)},
+                   "read_ceiling": {"128MiB": round(ceil_small, 1), "8GiB": round(ceil_big, 1),
+                                    "kind": "plain 16-byte-load read kernel, cold clean cache"},
+                   "frac_of_read_ceiling": {"batched": round(db_gbps / ceil_big, 4),
+                                            "single": round(ds_gbps / ceil_small, 4)}},
         "roofline": {
             "kernel": "fwd_bf16_kernel<128, causal>",
             "bound": "mfma",

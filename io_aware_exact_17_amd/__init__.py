@@ -36,6 +36,7 @@ SIGNATURES = {
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
+    "fa_probe_read": (_I, [_P, _Z, _P, _P]),
 }
 
 _lib = None
@@ -180,3 +181,21 @@ def fa_decode_varlen(q, kcache, vcache, seqlens, offsets, max_seqlen, scale=None
                               int(split_keys), pw, workspace.numel(), _stream(q, stream))
     _check(st, "fa_decode_varlen")
     return out, lse
+
+
+def fa_probe_read(buf, nbytes=None, sink=None, stream=None):
+    """Measurement aid (include/fa_probe.h): a plain streaming read of the first
+    `nbytes` bytes (default: all) of the contiguous device tensor `buf`."""
+    import torch
+
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    total = buf.numel() * buf.element_size()
+    n = total if nbytes is None else int(nbytes)
+    if n > total:
+        raise ValueError("nbytes exceeds the buffer")
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device=buf.device)
+    st = load().fa_probe_read(ctypes.c_void_p(buf.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+                              _stream(buf, stream))
+    _check(st, "fa_probe_read")

@@ -10,7 +10,8 @@ import pytest
 import io_aware_exact_17_amd as fa
 from conftest import ROOT, gpu_available
 
-HEADER = os.path.join(ROOT, "include", "fa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
 
 # Fake, suitably aligned device addresses: never dereferenced, because every
@@ -21,9 +22,11 @@ A2 = 0x20000
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exists_and_loads():
@@ -132,3 +135,13 @@ def test_binding_validates_tensors():
         fa.fa_fwd(q, q, q)  # host tensors are refused
     with pytest.raises(TypeError):
         fa.fa_fwd(None, q, q)
+
+
+def test_probe_rejects_invalid_arguments():
+    lib = fa.load()
+    assert lib.fa_probe_read(None, 1024, A2, None) == INVALID
+    assert lib.fa_probe_read(A, 1024, None, None) == INVALID
+    assert lib.fa_probe_read(A, 0, A2, None) == INVALID
+    assert lib.fa_probe_read(A, 1000, A2, None) == INVALID  # not a multiple of 16
+    assert lib.fa_probe_read(A + 8, 1024, A2, None) == INVALID
+

@@ -243,3 +243,15 @@ def test_decode_workspace_reused_across_calls(fa):
         torch.cuda.synchronize()
         O, L = oracle.decode(q, kc, vc, sl.cpu(), off.cpu(), 0.088)
         check(o, lse, O, L, TOL_BF16, f"reuse call {call}")
+
+
+def test_probe_read_runs(fa):
+    """The read probe (a measurement aid) streams a buffer and leaves the sink
+    alone unless the data's XOR hits its fixed constant (zeros never do)."""
+    log("case probe read")
+    buf = torch.zeros(3 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    fa.fa_probe_read(buf, sink=sink)
+    fa.fa_probe_read(buf, nbytes=4096 + 16, sink=sink)  # a ragged last workgroup
+    torch.cuda.synchronize()
+    assert sink.item() == 7
