@@ -7,6 +7,8 @@ One step is one pass of the whole hot path over resident synthetic inputs:
   2. fa_decode_varlen  batched decode, 64 sequences x 32 heads, d=128, history
                  lengths uniform in [128, 16384] (packed bf16 K/V cache)
   3. fa_decode_varlen  single-request decode, 32 heads, 8192-token history
+  4. fa_decode_paged   the batched decode's cache as 16-token pages in seeded
+                 random order (block table per sequence)
 The batched decode streams ~8.7 GB, far more than the 256 MB last-level
 cache, so the single-request decode that follows reads its 128 MiB of K/V
 from HBM.  Every call is bracketed by HIP events on the stream it runs on.
@@ -153,6 +155,18 @@ def main():
     ds_ws = torch.empty(fa.fa_decode_workspace_bytes(DS.B, DS.H, DS.d, DS.max_len, 0),
                         dtype=torch.uint8, device=dev)
 
+    # The batched workload again as a paged cache (16-token pages, random order).
+    PAGE = 16
+    pg_bt, pg_pages = W.paged_layout(dbl.cpu(), PAGE, seed=DB.seed, max_len=DB.max_len)
+    pg_k = W.to_pages(dbk, dbl, dbo, pg_bt, PAGE, pg_pages)
+    pg_v = W.to_pages(dbv, dbl, dbo, pg_bt, PAGE, pg_pages)
+    pg_bt = pg_bt.to(dev)
+    pg_sk = fa.fa_decode_paged_split_keys(DB.B, DB.H, DB.d, DB.max_len, PAGE)
+    pg_ws = torch.empty(fa.fa_decode_workspace_bytes(DB.B, DB.H, DB.d, DB.max_len, pg_sk),
+                        dtype=torch.uint8, device=dev)
+    pg_out = torch.empty_like(dbq)
+    pg_lse = torch.empty(DB.B, DB.H, dtype=torch.float32, device=dev)
+
     # A plain copy of known size, untimed: its HBM counters calibrate the
     # prefill kernel's FETCH_SIZE / WRITE_SIZE when this script runs under
     # rocprofv3 --pmc.
@@ -166,7 +180,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(rec):
-        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        e0, e1, e2, e3, e4 = ev(), ev(), ev(), ev(), ev()
         e0.record(stream)
         fa.fa_fwd(q, k, v, P.scale, True, out=o, lse=lse)
         e1.record(stream)
@@ -176,8 +190,11 @@ def main():
         fa.fa_decode_varlen(dsq, dsk, dsv, dsl, dso, DS.max_len, DS.scale, 0, out=ds_out,
                             lse=ds_lse, workspace=ds_ws)
         e3.record(stream)
+        fa.fa_decode_paged(dbq, pg_k, pg_v, pg_bt, dbl, DB.max_len, DB.scale, 0, out=pg_out,
+                           lse=pg_lse, workspace=pg_ws)
+        e4.record(stream)
         if rec is not None:
-            rec.append((e0, e1, e2, e3))
+            rec.append((e0, e1, e2, e3, e4))
 
     for _ in range(args.warmup):
         step(None)
@@ -191,9 +208,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    t_pre = [a.elapsed_time(b) for a, b, _, _ in recs]
-    t_db = [b.elapsed_time(c) for _, b, c, _ in recs]
-    t_ds = [c.elapsed_time(d) for _, _, c, d in recs]
+    t_pre = [r[0].elapsed_time(r[1]) for r in recs]
+    t_db = [r[1].elapsed_time(r[2]) for r in recs]
+    t_ds = [r[2].elapsed_time(r[3]) for r in recs]
+    t_pg = [r[3].elapsed_time(r[4]) for r in recs]
     ms_step = wall * 1e3 / args.steps
 
     flops = P.flops()
@@ -203,6 +221,7 @@ def main():
     ds_bytes = W.decode_kv_bytes(dsl.cpu(), DS.H, DS.d)
     db_gbps = db_bytes / (statistics.mean(t_db) * 1e-3) / 1e9
     ds_gbps = ds_bytes / (statistics.mean(t_ds) * 1e-3) / 1e9
+    pg_gbps = db_bytes / (statistics.mean(t_pg) * 1e-3) / 1e9
 
     ceil_small, ceil_big = read_ceiling(torch, fa, dev, stream, ds_bytes)
 
@@ -223,7 +242,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "causal prefill B=1 H=32 N=8192 d=128 + batched varlen decode "
-                        "64 seqs x 32 heads d=128 len U[128,16384] + single decode H=32 N=8192 d=128",
+                        "64 seqs x 32 heads d=128 len U[128,16384] + single decode H=32 N=8192 d=128 "
+                        "+ the batched decode over a paged cache (16-token pages)",
             "prefill": {"B": P.B, "H": P.H, "Nq": P.Nq, "Nk": P.Nk, "d": P.d, "causal": True,
                         "seed": P.seed, "flops": flops, "ms_mean": round(pre_ms, 4),
                         "ms_median": round(statistics.median(t_pre), 4),
@@ -234,16 +254,21 @@ def main():
             "decode_single": {"B": DS.B, "H": DS.H, "Nk": DS.fixed_len, "d": DS.d,
                               "kv_bytes": ds_bytes, "split_keys": ds_sk,
                               "ms_mean": round(statistics.mean(t_ds), 4)},
+            "decode_paged": {"page_size": PAGE, "pages": pg_pages, "split_keys": pg_sk,
+                             "kv_bytes": db_bytes, "ms_mean": round(statistics.mean(t_pg), 4)},
         },
         "decode": {"unit": "GB/s",
                    "batched_kv_read": round(db_gbps, 1),
                    "single_kv_read": round(ds_gbps, 1),
+                   "paged_batched_kv_read": round(pg_gbps, 1),
                    "frac_of_hbm_peak": {"batched": round(db_gbps / PEAK_HBM_GBPS, 4),
-                                        "single": round(ds_gbps / PEAK_HBM_GBPS, 4)},
+                                        "single": round(ds_gbps / PEAK_HBM_GBPS, 4),
+                                        "paged_batched": round(pg_gbps / PEAK_HBM_GBPS, 4)},
                    "read_ceiling": {"128MiB": round(ceil_small, 1), "8GiB": round(ceil_big, 1),
                                     "kind": "plain 16-byte-load read kernel, cold clean cache"},
                    "frac_of_read_ceiling": {"batched": round(db_gbps / ceil_big, 4),
-                                            "single": round(ds_gbps / ceil_small, 4)}},
+                                            "single": round(ds_gbps / ceil_small, 4),
+                                            "paged_batched": round(pg_gbps / ceil_big, 4)}},
         "roofline": {
             "kernel": "fwd_bf16_kernel<128, causal>",
             "bound": "mfma",

@@ -130,6 +130,44 @@ int fa_decode_varlen(const void* q, const void* kcache, const void* vcache,
                      void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/*
+ * Decode over a paged KV cache (explainer §6 names paging as the concern of
+ * batched decode): the same computation as fa_decode_varlen, but the cache is
+ * a pool of fixed-size pages and each sequence lists its pages in a block
+ * table.  Key t of sequence b is in page block_table[b * max_blocks + t /
+ * page_size], slot t % page_size.
+ *
+ *   q            bf16 [B, H, d]                         (device)
+ *   kpages       bf16 [num_pages, page_size, H, d]      (device)
+ *   vpages       bf16 [num_pages, page_size, H, d]      (device)
+ *   block_table  int32 [B, max_blocks]                  (device); entries
+ *                j < ceil(seqlens[b] / page_size) must lie in [0, num_pages)
+ *                (an entry outside reads page num_pages - 1 instead of
+ *                faulting; later entries are never read)
+ *   seqlens      int32 [B]                              (device)
+ *   o, lse, max_seqlen, scale, workspace: as for fa_decode_varlen (the same
+ *                fa_decode_workspace_bytes sizes the workspace)
+ *   page_size    tokens per page, a power of two, 1 .. 65536
+ *   max_blocks   entries per block-table row; max_blocks * page_size >=
+ *                max_seqlen, else FA_ERR_INVALID_ARG
+ *   split_keys   as for fa_decode_varlen, and a chunk may span at most 1024
+ *                pages (ceil(split_keys / page_size) + 1 <= 1024); 0 lets the
+ *                library choose, as fa_decode_paged_split_keys reports (size
+ *                the workspace with that value)
+ *
+ * fa_decode_paged_split_keys: the chunk size the library picks for split_keys
+ * = 0 (the packed plan, halved while a chunk would span more than 1024
+ * pages); 0 for invalid arguments.
+ */
+int fa_decode_paged_split_keys(int B, int H, int d, int max_seqlen, int page_size);
+int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
+                    const int32_t* block_table, const int32_t* seqlens,
+                    void* o, float* lse,
+                    int B, int H, int d, int page_size, int num_pages, int max_blocks,
+                    int max_seqlen, float scale, int split_keys,
+                    void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_string(int status);
 

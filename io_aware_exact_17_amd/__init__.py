@@ -9,6 +9,7 @@ exception is raised.
     o, lse = fa_fwd(q, k, v, scale, causal)            # bf16 [B,H,N,d]
     o, lse = fa_fwd_f32(q, k, v, scale, causal)        # fp32 [B,H,N,d]
     o, lse = fa_decode_varlen(q, kcache, vcache, seqlens, offsets, max_seqlen, scale)
+    o, lse = fa_decode_paged(q, kpages, vpages, block_table, seqlens, max_seqlen, scale)
 """
 from __future__ import annotations
 
@@ -36,6 +37,9 @@ SIGNATURES = {
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
+    "fa_decode_paged_split_keys": (_I, [_I, _I, _I, _I, _I]),
+    "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P,
+                             _Z, _P]),
     "fa_probe_read": (_I, [_P, _Z, _P, _P]),
 }
 
@@ -180,6 +184,50 @@ def fa_decode_varlen(q, kcache, vcache, seqlens, offsets, max_seqlen, scale=None
     st = lib.fa_decode_varlen(pq, pk, pv, ps, po_, po, pl, B, H, d, int(max_seqlen), float(scale),
                               int(split_keys), pw, workspace.numel(), _stream(q, stream))
     _check(st, "fa_decode_varlen")
+    return out, lse
+
+
+def fa_decode_paged_split_keys(B, H, d, max_seqlen, page_size) -> int:
+    return int(load().fa_decode_paged_split_keys(B, H, d, max_seqlen, page_size))
+
+
+def fa_decode_paged(q, kpages, vpages, block_table, seqlens, max_seqlen, scale=None, split_keys=0,
+                    out=None, lse=None, workspace=None, stream=None):
+    """Decode over a paged cache: q [B,H,d], kpages/vpages [num_pages,page_size,H,d]
+    bf16, block_table int32 [B,max_blocks] and seqlens int32 [B] on the device;
+    max_seqlen a host int >= every seqlens[b].  Returns (O bf16 [B,H,d], LSE
+    fp32 [B,H])."""
+    import torch
+
+    lib = load()
+    pq = _dev(q, "q", torch.bfloat16, 3)
+    pk = _dev(kpages, "kpages", torch.bfloat16, 4)
+    pv = _dev(vpages, "vpages", torch.bfloat16, 4)
+    pb = _dev(block_table, "block_table", torch.int32, 2)
+    ps = _dev(seqlens, "seqlens", torch.int32, 1)
+    B, H, d = q.shape
+    num_pages, page_size = kpages.shape[0], kpages.shape[1]
+    if kpages.shape[2:] != (H, d) or vpages.shape != kpages.shape:
+        raise ValueError("page pool shape mismatch")
+    if block_table.shape[0] != B or seqlens.shape[0] != B:
+        raise ValueError("block_table / seqlens must have B rows")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    po = _dev(out, "out", torch.bfloat16, 3)
+    pl = _dev(lse, "lse", torch.float32, 2)
+    sk = int(split_keys) or fa_decode_paged_split_keys(B, H, d, int(max_seqlen), int(page_size))
+    need = fa_decode_workspace_bytes(B, H, d, int(max_seqlen), sk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    pw = _dev(workspace, "workspace", torch.uint8, 1)
+    st = lib.fa_decode_paged(pq, pk, pv, pb, ps, po, pl, B, H, d, int(page_size), int(num_pages),
+                             int(block_table.shape[1]), int(max_seqlen), float(scale),
+                             int(split_keys), pw, workspace.numel(), _stream(q, stream))
+    _check(st, "fa_decode_paged")
     return out, lse
 
 

@@ -13,6 +13,8 @@ namespace {
 constexpr long long kMaxGridX = 0x7fffffffLL;  // HIP grid.x limit
 constexpr long long kMaxGridYZ = 65535;
 constexpr long long kMaxChunks = 256;  // chunks per sequence the merge kernel combines
+constexpr long long kMaxPageSize = 1 << 16;   // tokens per page of a paged cache
+constexpr long long kMaxChunkPages = 1024;    // pages one chunk may span (staged in LDS)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -51,9 +53,27 @@ int choose_split_keys(int B, int H, int max_seqlen) {
   return (int)sk;
 }
 
+// The packed plan, halved while a chunk would span more pages than the
+// kernel stages in LDS.
+int choose_paged_split_keys(int B, int H, int max_seqlen, int page_size) {
+  long long sk = choose_split_keys(B, H, max_seqlen);
+  while ((sk + page_size - 1) / page_size + 1 > kMaxChunkPages && sk > 64) sk /= 2;
+  return (int)sk;
+}
+
+bool page_size_ok(int page_size) {
+  return page_size >= 1 && page_size <= kMaxPageSize && (page_size & (page_size - 1)) == 0;
+}
+
 }  // namespace
 
 extern "C" {
+
+int fa_decode_paged_split_keys(int B, int H, int d, int max_seqlen, int page_size) {
+  (void)d;
+  if (B < 1 || H < 1 || max_seqlen < 1 || !page_size_ok(page_size)) return 0;
+  return choose_paged_split_keys(B, H, max_seqlen, page_size);
+}
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
            int Nk, int d, float scale, int causal, hipStream_t stream) {
@@ -97,8 +117,40 @@ int fa_decode_varlen(const void* q, const void* kcache, const void* vcache, cons
   if (n_splits > kMaxChunks) return FA_ERR_INVALID_ARG;
   const size_t need = fa_decode_workspace_bytes(B, H, d, max_seqlen, sk);
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  fa::DecodeArgs a{q, kcache, vcache, seqlens, offsets, o, lse, B, H, d, max_seqlen, scale,
+  fa::DecodeArgs a{q,  kcache, vcache, seqlens, offsets, nullptr,   0,  0,
+                   0,  o,      lse,    B,       H,       d,         max_seqlen, scale,
                    sk, (int)n_splits, static_cast<float*>(workspace), stream};
+  return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
+                    const int32_t* block_table, const int32_t* seqlens, void* o, float* lse, int B,
+                    int H, int d, int page_size, int num_pages, int max_blocks, int max_seqlen,
+                    float scale, int split_keys, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  if (!q || !kpages || !vpages || !block_table || !seqlens || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kpages) || !aligned16(vpages) || !aligned4(o) ||
+      !aligned4(lse) || !aligned4(seqlens) || !aligned4(block_table))
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || max_seqlen < 1 || num_pages < 1 || max_blocks < 1) return FA_ERR_INVALID_ARG;
+  if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_INVALID_ARG;  // grid.z / grid.x
+  if (!page_size_ok(page_size)) return FA_ERR_INVALID_ARG;
+  if ((long long)max_blocks * page_size < max_seqlen) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (split_keys < 0 || split_keys % 64 != 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const long long sk = split_keys > 0 ? split_keys : choose_paged_split_keys(B, H, max_seqlen, page_size);
+  // a chunk that starts inside a page spans one page more than its length needs
+  if ((sk + page_size - 1) / page_size + 1 > kMaxChunkPages) return FA_ERR_INVALID_ARG;
+  const long long n_splits = ((long long)max_seqlen + sk - 1) / sk;
+  if (n_splits > kMaxChunks || n_splits > kMaxGridYZ) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, max_seqlen, (int)sk);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  fa::DecodeArgs a{q,  kpages, vpages,     seqlens, nullptr, block_table, max_blocks, shift,
+                   num_pages, o, lse,      B,       H,       d,           max_seqlen, scale,
+                   (int)sk, (int)n_splits, static_cast<float*>(workspace), stream};
   return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -27,6 +27,7 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxChunkPages = 1024;  // pages one chunk may span (paged cache)
 
 template <int D>
 struct DecCfg {
@@ -52,10 +53,15 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <int D>
+// PAGED: the cache is a pool of pages [num_pages, page_size, H, d] and
+// sequence b's key t lives in page block_table[b][t / page_size], slot
+// t % page_size (page_size a power of two); otherwise the cache is packed
+// and sequence b owns rows offsets[b] ...
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ seqlens, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ block_table, int bt_stride, int page_shift, int num_pages,
     bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ ws_u,
     float* __restrict__ ws_ml, int H, int split_keys, int n_splits, float c) {
   using C = DecCfg<D>;
@@ -76,7 +82,29 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
   if (k_begin >= len) return;  // chunk past this sequence's end
   const int k_end = min(len, k_begin + split_keys);
   const int n_active = min(n_splits, (len + split_keys - 1) / split_keys);
-  const size_t base = (size_t)offsets[b];
+  // Cache row of the sequence's key kk.  Paged: the chunk's page numbers are
+  // staged in LDS once (entries out of range read the last page instead of
+  // faulting), then every key costs an LDS read, a shift and an add.
+  __shared__ int sm_page[PAGED ? kMaxChunkPages : 1];
+  size_t base = 0;
+  int p0 = 0;
+  if constexpr (PAGED) {
+    p0 = k_begin >> page_shift;
+    const int np = ((k_end - 1) >> page_shift) - p0 + 1;
+    const int32_t* bt = block_table + (size_t)b * bt_stride + p0;
+    for (int i = tid; i < np; i += kThreads)
+      sm_page[i] = (int)min((unsigned)bt[i], (unsigned)(num_pages - 1));
+    __syncthreads();
+  } else {
+    base = (size_t)offsets[b];
+  }
+  const int page_mask = (1 << page_shift) - 1;
+  auto row_of = [&](int kk) -> size_t {
+    if constexpr (PAGED)
+      return ((size_t)sm_page[(kk >> page_shift) - p0] << page_shift) + (size_t)(kk & page_mask);
+    else
+      return base + (size_t)kk;
+  };
 
   const int sub = tid % C::LPR;  // which 8 dims of the row this lane reads
   const int rg = tid / C::LPR;   // lane group
@@ -111,8 +139,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     for (int i = 0; i < C::U; ++i) {
       int kk = k0 + C::NRG * i;
       kk = kk < k_end ? kk : k_begin;
-      kr[i] = *reinterpret_cast<const u32x4*>(kp + (base + kk) * row_stride);
-      vr[i] = *reinterpret_cast<const u32x4*>(vp + (base + kk) * row_stride);
+      const size_t row = row_of(kk);
+      kr[i] = *reinterpret_cast<const u32x4*>(kp + row * row_stride);
+      vr[i] = *reinterpret_cast<const u32x4*>(vp + row * row_stride);
     }
   };
   auto consume = [&](const u32x4 (&kr)[C::U], const u32x4 (&vr)[C::U], int k0) {
@@ -266,18 +295,21 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(
   }
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch(const DecodeArgs& a) {
   const float c = a.scale * kLog2e;
   float* ws_u = a.ws;
   float* ws_ml = ws_u + (size_t)a.B * a.H * a.n_splits * D;
   {
-    void* args[] = {(void*)&a.q, (void*)&a.kcache, (void*)&a.vcache, (void*)&a.seqlens,
-                    (void*)&a.offsets, (void*)&a.o, (void*)&a.lse, (void*)&ws_u, (void*)&ws_ml,
-                    (void*)&a.H, (void*)&a.split_keys, (void*)&a.n_splits, (void*)&c};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<D>),
-                                         dim3((unsigned)a.H, (unsigned)a.n_splits, (unsigned)a.B),
-                                         dim3(kThreads), args, 0, a.stream);
+    void* args[] = {(void*)&a.q,          (void*)&a.kcache,    (void*)&a.vcache,
+                    (void*)&a.seqlens,    (void*)&a.offsets,   (void*)&a.block_table,
+                    (void*)&a.bt_stride,  (void*)&a.page_shift, (void*)&a.num_pages,
+                    (void*)&a.o,          (void*)&a.lse,       (void*)&ws_u,
+                    (void*)&ws_ml,        (void*)&a.H,         (void*)&a.split_keys,
+                    (void*)&a.n_splits,   (void*)&c};
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void*>(&decode_split_kernel<D, PAGED>),
+        dim3((unsigned)a.H, (unsigned)a.n_splits, (unsigned)a.B), dim3(kThreads), args, 0, a.stream);
     if (e != hipSuccess) return e;
   }
   if (a.n_splits == 1) return hipSuccess;  // every sequence finished in the split kernel
@@ -290,7 +322,9 @@ hipError_t launch(const DecodeArgs& a) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a) {
-  return a.d == 128 ? launch<128>(a) : launch<64>(a);
+  if (a.block_table)
+    return a.d == 128 ? launch<128, true>(a) : launch<64, true>(a);
+  return a.d == 128 ? launch<128, false>(a) : launch<64, false>(a);
 }
 
 }  // namespace fa

@@ -25,7 +25,11 @@ struct DecodeArgs {
   const void* kcache;
   const void* vcache;
   const int32_t* seqlens;
-  const int32_t* offsets;
+  const int32_t* offsets;       // packed cache (null when paged)
+  const int32_t* block_table;   // paged cache: [B, bt_stride] page numbers (null when packed)
+  int bt_stride;                // entries per block-table row
+  int page_shift;               // log2(page_size)
+  int num_pages;                // pages in the pool
   void* o;
   float* lse;
   int B, H, d, max_seqlen;

@@ -152,3 +152,35 @@ def decode(q, kcache, vcache, seqlens, offsets, scale, heads=None, seqs=None):
             O[b, h] = o[0]
             L[b, h] = lse[0]
     return O, L
+
+
+def decode_paged(q, kpages, vpages, block_table, seqlens, scale, heads=None, seqs=None):
+    """Exact single-query attention over a paged cache.
+
+    kpages, vpages: [num_pages, page_size, H, d]; block_table: [B, max_blocks].
+    Key t of sequence b sits in page block_table[b, t // page_size] at slot
+    t % page_size (the block table maps a sequence's logical blocks to the
+    physical pages that hold them).  The sequence's keys are gathered in
+    order and attended exactly as in `decode`.
+
+    Returns O [B, H, d] and LSE [B, H], float64."""
+    B, H, d = q.shape
+    page_size = kpages.shape[1]
+    bt = np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table)
+    O = np.full((B, H, vpages.shape[-1]), np.nan)
+    L = np.full((B, H), np.nan)
+    seqs = range(B) if seqs is None else seqs
+    heads = range(H) if heads is None else heads
+    for b in seqs:
+        n = int(seqlens[b])
+        t = np.arange(n)
+        page = bt[b, t // page_size]
+        slot = t % page_size
+        for h in heads:
+            Kb = _f64(kpages[page, slot, h]) if n else np.zeros((0, d))
+            Vb = _f64(vpages[page, slot, h]) if n else np.zeros((0, vpages.shape[-1]))
+            o, lse = head_attention(_f64(q[b, h])[None, :], Kb, Vb, scale)
+            O[b, h] = o[0]
+            L[b, h] = lse[0]
+    return O, L
+

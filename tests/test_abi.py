@@ -145,3 +145,35 @@ def test_probe_rejects_invalid_arguments():
     assert lib.fa_probe_read(A, 1000, A2, None) == INVALID  # not a multiple of 16
     assert lib.fa_probe_read(A + 8, 1024, A2, None) == INVALID
 
+
+def paged_call(q=A, kp=A, vp=A, bt=A2, sl=A2, o=A2, lse=A2, B=2, H=4, d=128, page=16,
+               num_pages=100, max_blocks=8, max_seqlen=100, scale=0.1, split_keys=0,
+               ws=A, ws_bytes=1 << 30):
+    lib = fa.load()
+    return lib.fa_decode_paged(q, kp, vp, bt, sl, o, lse, B, H, d, page, num_pages, max_blocks,
+                               max_seqlen, scale, split_keys, ws, ws_bytes, None)
+
+
+def test_decode_paged_rejects_invalid_arguments():
+    assert paged_call(bt=None) == INVALID
+    assert paged_call(kp=A + 4) == INVALID
+    assert paged_call(bt=A2 + 2) == INVALID
+    for page in (0, 3, 48, 1 << 17):
+        assert paged_call(page=page) == INVALID, page
+    assert paged_call(num_pages=0) == INVALID
+    assert paged_call(max_blocks=6) == INVALID           # 6 * 16 < 100 keys
+    assert paged_call(page=1, max_blocks=100, split_keys=2048) == INVALID  # 2049 pages per chunk
+    assert paged_call(split_keys=96) == INVALID
+    assert paged_call(d=96) == UNSUPPORTED
+    assert paged_call(ws=None) == WORKSPACE
+    need = fa.fa_decode_workspace_bytes(2, 4, 128, 100, fa.fa_decode_paged_split_keys(2, 4, 128, 100, 16))
+    assert paged_call(ws_bytes=need - 1) == WORKSPACE
+
+
+def test_decode_paged_split_plan():
+    # pages of 16 keep the packed plan; single-key pages shrink the chunk to fit 1024 pages
+    assert fa.fa_decode_paged_split_keys(1, 32, 128, 8192, 16) == fa.fa_decode_split_keys(1, 32, 128, 8192)
+    sk = fa.fa_decode_paged_split_keys(1, 1, 128, 1 << 20, 1)
+    assert sk % 64 == 0 and sk + 1 <= 1024
+    assert fa.fa_decode_paged_split_keys(1, 1, 128, 100, 3) == 0
+

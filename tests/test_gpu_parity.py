@@ -245,6 +245,59 @@ def test_decode_workspace_reused_across_calls(fa):
         check(o, lse, O, L, TOL_BF16, f"reuse call {call}")
 
 
+def paged_copy(kc, vc, sl, off, page_size, seed, spare=3, max_len=None):
+    bt, npg = W.paged_layout(sl, page_size, seed=seed, spare_pages=spare, max_len=max_len)
+    kp = W.to_pages(kc, sl, off, bt, page_size, npg)
+    vp = W.to_pages(vc, sl, off, bt, page_size, npg)
+    return bt, kp, vp
+
+
+@pytest.mark.parametrize("d,P,sk", [(128, 1, 64), (128, 16, 0), (128, 16, 256), (128, 64, 128),
+                                    (128, 256, 0), (128, 4096, 0), (64, 32, 0)])
+def test_decode_paged(fa, d, P, sk):
+    """Paged cache, pages in random order: against the oracle, and identical
+    to the packed kernel run with the same chunks (same arithmetic, only the
+    addresses differ)."""
+    lens = [0, 1, max(P - 1, 2), P, P + 1, 700, 3000]
+    B, H = len(lens), 4
+    log(f"case decode paged d={d} page={P} split_keys={sk}")
+    q, kc, vc, sl, off = W.decode_inputs(B, H, d, lens, seed=50 + P, device="cuda")
+    bt, kp, vp = paged_copy(kc, vc, sl, off, P, seed=P)
+    o, lse = fa.fa_decode_paged(q, kp, vp, bt.to("cuda"), sl, max(lens), 0.088, sk)
+    sk_used = sk or fa.fa_decode_paged_split_keys(B, H, d, max(lens), P)
+    o2, lse2 = fa.fa_decode_varlen(q, kc, vc, sl, off, max(lens), 0.088, sk_used)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_paged(q, kp, vp, bt, sl.cpu(), 0.088)
+    check(o, lse, O, L, TOL_BF16, f"paged page={P}")
+    assert torch.equal(o, o2), "paged and packed outputs differ"
+    assert torch.equal(lse.isneginf(), lse2.isneginf())
+    fin = ~lse.isneginf()
+    assert torch.equal(lse[fin], lse2[fin]), "paged and packed LSE differ"
+
+
+def test_decode_paged_batched_full_size(fa):
+    """The batched decode workload (64 sequences, lengths U[128, 16384]) with
+    16-token pages in random order: whole output identical to the packed
+    kernel, sampled (sequence, head) pairs against the oracle."""
+    s = W.DECODE_BATCHED
+    log(f"case {s.name} paged 16")
+    q, kc, vc, sl, off = W.decode_spec_inputs(s, "cuda")
+    bt, kp, vp = paged_copy(kc, vc, sl, off, 16, seed=s.seed, max_len=s.max_len)
+    del kc, vc
+    o, lse = fa.fa_decode_paged(q, kp, vp, bt.to("cuda"), sl, s.max_len, s.scale, 0)
+    torch.cuda.synchronize()
+    seqs, heads = [0, 7, 31, 63], [0, 13, 31]
+    O, L = oracle.decode_paged(q, kp, vp, bt, sl.cpu(), s.scale, heads=heads, seqs=seqs)
+    idx = np.ix_(seqs, heads)
+    check(o[seqs][:, heads], lse[seqs][:, heads], O[idx], L[idx], TOL_BF16, "paged batched sampled")
+    del kp, vp
+    q2, kc, vc, sl2, off2 = W.decode_spec_inputs(s, "cuda")
+    sk = fa.fa_decode_paged_split_keys(s.B, s.H, s.d, s.max_len, 16)
+    o2, lse2 = fa.fa_decode_varlen(q2, kc, vc, sl2, off2, s.max_len, s.scale, sk)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
 def test_probe_read_runs(fa):
     """The read probe (a measurement aid) streams a buffer and leaves the sink
     alone unless the data's XOR hits its fixed constant (zeros never do)."""

@@ -301,3 +301,48 @@ def test_planted_mistake_is_caught(name):
         except (AssertionError, ValueError, IndexError, FloatingPointError):
             failed.append(pin.__name__)
     assert failed, f"mutation {name} slipped past every pin"
+
+
+def _pages_by_hand(cache, lens, offs, bt, P, num_pages):
+    """A page pool filled one token at a time from the block-table definition."""
+    T, H, d = cache.shape
+    pool = np.zeros((num_pages, P, H, d))
+    for b, n in enumerate(lens):
+        for t in range(n):
+            pool[bt[b][t // P], t % P] = cache[offs[b] + t]
+    return pool
+
+
+@pytest.mark.parametrize("P", [1, 3, 16, 64])
+def test_paged_decode_oracle_is_packed_decode(P):
+    """Paging only moves keys around: gathering a sequence's keys through any
+    block table gives the packed decode exactly (the packed oracle is pinned
+    to the forward definition above)."""
+    rng = np.random.default_rng(17 + P)
+    lens = [0, 1, P, P + 1, 3 * P - 1, 40]
+    B, H, d = len(lens), 2, 8
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(int)
+    T = int(sum(lens))
+    kc, vc = rng.standard_normal((T, H, d)), rng.standard_normal((T, H, d))
+    q = rng.standard_normal((B, H, d))
+    need = [-(-n // P) for n in lens]
+    num_pages = sum(need) + 3
+    order = rng.permutation(num_pages)
+    bt = np.full((B, max(need)), -1)
+    at = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = order[at:at + n]
+        at += n
+    kp = _pages_by_hand(kc, lens, offs, bt, P, num_pages)
+    vp = _pages_by_hand(vc, lens, offs, bt, P, num_pages)
+    O1, L1 = oracle.decode(q, kc, vc, lens, offs, 0.3)
+    O2, L2 = oracle.decode_paged(q, kp, vp, bt, lens, 0.3)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    # a block-table entry pointing at another sequence's page is noticed
+    # (swapping two of a sequence's own pages would not be: with every key
+    # visible, attention does not depend on key order)
+    b, other = lens.index(3 * P - 1), lens.index(40)
+    bad = bt.copy()
+    bad[b, 0] = bt[other, 0]
+    O3, _ = oracle.decode_paged(q, kp, vp, bad, lens, 0.3)
+    assert not np.allclose(O3[b], O1[b])

@@ -139,6 +139,48 @@ def decode_spec_inputs(spec: DecodeSpec, device="cpu"):
     return decode_inputs(spec.B, spec.H, spec.d, lens, spec.seed, device)
 
 
+def paged_layout(seqlens, page_size, seed=0, spare_pages=0, max_len=None):
+    """A block table for a paged cache: sequence b needs ceil(len_b / page_size)
+    pages, and all pages (plus `spare_pages` never referenced) are handed out
+    in a seeded random order.  The table has room for `max_len` keys per
+    sequence (default: the longest).  Returns (block_table int32
+    [B, max_blocks] on the host, unreferenced entries -1, and num_pages)."""
+    lens = [int(x) for x in torch.as_tensor(seqlens).cpu()]
+    need = [-(-n // page_size) for n in lens]
+    num_pages = max(sum(need) + spare_pages, 1)
+    perm = torch.randperm(num_pages, generator=_gen("cpu", seed + 104729)).to(torch.int32)
+    cols = max(max(need), -(-int(max_len) // page_size) if max_len else 0, 1)
+    bt = torch.full((len(lens), cols), -1, dtype=torch.int32)
+    at = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = perm[at:at + n]
+        at += n
+    return bt, num_pages
+
+
+def to_pages(cache, seqlens, offsets, block_table, page_size, num_pages):
+    """Copy a packed token-major cache [T, H, d] into a page pool
+    [num_pages, page_size, H, d] laid out by `block_table` (slots no sequence
+    uses stay zero).  Runs on the cache's device."""
+    dev = cache.device
+    T, H, d = cache.shape
+    pool = torch.zeros((num_pages * page_size, H, d), dtype=cache.dtype, device=dev)
+    lens = torch.as_tensor(seqlens).cpu().to(torch.int64)
+    offs = torch.as_tensor(offsets).cpu().to(torch.int64)
+    bt = torch.as_tensor(block_table).cpu().to(torch.int64)
+    src, dst = [], []
+    for b in range(len(lens)):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        t = torch.arange(n)
+        src.append(offs[b] + t)
+        dst.append(bt[b, t // page_size] * page_size + t % page_size)
+    if src:
+        pool[torch.cat(dst).to(dev)] = cache[torch.cat(src).to(dev)]
+    return pool.view(num_pages, page_size, H, d)
+
+
 def decode_kv_bytes(seqlens, H, d, elem_bytes=2) -> int:
     """Bytes of K plus V history the decode step must read."""
     T = int(torch.as_tensor(seqlens).to(torch.int64).sum())
