@@ -9,6 +9,8 @@ One step is one pass of the whole hot path over resident synthetic inputs:
   3. fa_decode_varlen  single-request decode, 32 heads, 8192-token history
   4. fa_decode_paged   the batched decode's cache as 16-token pages in seeded
                  random order (block table per sequence)
+  5. fa_fwd_varlen     packed causal prefill of 8 sequences, lengths U[512, 8192],
+                 H=32, d=128 (token-major [T, H, d], cu_seqlens)
 The batched decode streams ~8.7 GB, far more than the 256 MB last-level
 cache, so the single-request decode that follows reads its 128 MiB of K/V
 from HBM.  Every call is bracketed by HIP events on the stream it runs on.
@@ -167,6 +169,14 @@ def main():
     pg_out = torch.empty_like(dbq)
     pg_lse = torch.empty(DB.B, DB.H, dtype=torch.float32, device=dev)
 
+    # Packed variable-length causal prefill.
+    VL = W.VARLEN_PREFILL
+    vl_lens, vlq, vlk, vlv, vlcq, vlck = W.varlen_spec_inputs(VL, dev)
+    vl_max = int(vl_lens.max())
+    vl_out = torch.empty_like(vlq)
+    vl_lse = torch.empty(VL.H, vlq.shape[0], dtype=torch.float32, device=dev)
+    vl_flops = VL.flops(vl_lens)
+
     # A plain copy of known size, untimed: its HBM counters calibrate the
     # prefill kernel's FETCH_SIZE / WRITE_SIZE when this script runs under
     # rocprofv3 --pmc.
@@ -180,7 +190,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(rec):
-        e0, e1, e2, e3, e4 = ev(), ev(), ev(), ev(), ev()
+        e0, e1, e2, e3, e4, e5 = ev(), ev(), ev(), ev(), ev(), ev()
         e0.record(stream)
         fa.fa_fwd(q, k, v, P.scale, True, out=o, lse=lse)
         e1.record(stream)
@@ -193,8 +203,11 @@ def main():
         fa.fa_decode_paged(dbq, pg_k, pg_v, pg_bt, dbl, DB.max_len, DB.scale, 0, out=pg_out,
                            lse=pg_lse, workspace=pg_ws)
         e4.record(stream)
+        fa.fa_fwd_varlen(vlq, vlk, vlv, vlcq, vlck, vl_max, VL.scale, VL.causal, out=vl_out,
+                         lse=vl_lse)
+        e5.record(stream)
         if rec is not None:
-            rec.append((e0, e1, e2, e3, e4))
+            rec.append((e0, e1, e2, e3, e4, e5))
 
     for _ in range(args.warmup):
         step(None)
@@ -212,6 +225,7 @@ def main():
     t_db = [r[1].elapsed_time(r[2]) for r in recs]
     t_ds = [r[2].elapsed_time(r[3]) for r in recs]
     t_pg = [r[3].elapsed_time(r[4]) for r in recs]
+    t_vl = [r[4].elapsed_time(r[5]) for r in recs]
     ms_step = wall * 1e3 / args.steps
 
     flops = P.flops()
@@ -222,6 +236,7 @@ def main():
     db_gbps = db_bytes / (statistics.mean(t_db) * 1e-3) / 1e9
     ds_gbps = ds_bytes / (statistics.mean(t_ds) * 1e-3) / 1e9
     pg_gbps = db_bytes / (statistics.mean(t_pg) * 1e-3) / 1e9
+    vl_tflops = vl_flops / (statistics.mean(t_vl) * 1e-3) / 1e12
 
     ceil_small, ceil_big = read_ceiling(torch, fa, dev, stream, ds_bytes)
 
@@ -243,7 +258,8 @@ def main():
         "config": {
             "workload": "causal prefill B=1 H=32 N=8192 d=128 + batched varlen decode "
                         "64 seqs x 32 heads d=128 len U[128,16384] + single decode H=32 N=8192 d=128 "
-                        "+ the batched decode over a paged cache (16-token pages)",
+                        "+ the batched decode over a paged cache (16-token pages) "
+                        "+ packed causal prefill 8 seqs x 32 heads d=128 len U[512,8192]",
             "prefill": {"B": P.B, "H": P.H, "Nq": P.Nq, "Nk": P.Nk, "d": P.d, "causal": True,
                         "seed": P.seed, "flops": flops, "ms_mean": round(pre_ms, 4),
                         "ms_median": round(statistics.median(t_pre), 4),
@@ -256,6 +272,9 @@ def main():
                               "ms_mean": round(statistics.mean(t_ds), 4)},
             "decode_paged": {"page_size": PAGE, "pages": pg_pages, "split_keys": pg_sk,
                              "kv_bytes": db_bytes, "ms_mean": round(statistics.mean(t_pg), 4)},
+            "prefill_varlen": {"B": VL.B, "H": VL.H, "d": VL.d, "causal": VL.causal,
+                               "seed": VL.seed, "lengths": [int(x) for x in vl_lens],
+                               "flops": vl_flops, "ms_mean": round(statistics.mean(t_vl), 4)},
         },
         "decode": {"unit": "GB/s",
                    "batched_kv_read": round(db_gbps, 1),
@@ -278,6 +297,8 @@ def main():
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": PREFILL_TRAFFIC_BYTES,
         },
+        "varlen": {"unit": "TFLOP/s", "prefill_varlen": round(vl_tflops, 2),
+                   "frac_of_bf16_peak": round(vl_tflops / PEAK_BF16_TFLOPS, 4)},
         "cpu_baseline": cpu,
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "torch": torch.__version__,

@@ -92,6 +92,34 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                hipStream_t stream);
 
 /*
+ * Forward over a packed batch of sequences of different lengths (variable
+ * length / padding-free prefill; the pages list padding masks among the
+ * semantics to get right).  Every sequence attends only within itself; with
+ * causal != 0 query i of a sequence with Lq queries and Lk keys sees key j iff
+ * j <= i + Lk - Lq (bottom-right: its queries are the last of its keys, as in
+ * a chunked prefill that appends Lq tokens to Lk - Lq cached ones).
+ *
+ *   q             bf16 [total_q, H, d]     token-major, contiguous (device)
+ *   k, v          bf16 [total_k, H, d]     (device)
+ *   o             bf16 [total_q, H, d]     written (device)
+ *   lse           fp32 [H, total_q]        written (device)
+ *   cu_seqlens_q  int32 [B + 1]            cu[0] = 0, non-decreasing,
+ *   cu_seqlens_k  int32 [B + 1]            cu[B] = total rows (device);
+ *                 sequence b owns rows cu[b] .. cu[b+1]-1
+ *   total_q       query rows (host); max_seqlen_q an upper bound of every
+ *                 sequence's query count (host; sizes the grid, no device
+ *                 read on the host), 1 <= max_seqlen_q <= total_q
+ *   d             64 or 128
+ *
+ * A query row that sees no key gets O = 0 and LSE = -inf.  Errors as for
+ * fa_fwd; the cu_seqlens contract is on the caller (device data).
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                  int B, int H, int d, int total_q, int max_seqlen_q, float scale, int causal,
+                  hipStream_t stream);
+
+/*
  * Decode: one new query per sequence over a packed, variable-length KV cache
  * (explainer §6: a single query sees its whole history; batched decode mixes
  * history lengths).  Each sequence's keys are cut into chunks of `split_keys`

@@ -8,6 +8,7 @@ exception is raised.
 
     o, lse = fa_fwd(q, k, v, scale, causal)            # bf16 [B,H,N,d]
     o, lse = fa_fwd_f32(q, k, v, scale, causal)        # fp32 [B,H,N,d]
+    o, lse = fa_fwd_varlen(q, k, v, cu_q, cu_k, max_q, scale, causal)  # packed [T,H,d]
     o, lse = fa_decode_varlen(q, kcache, vcache, seqlens, offsets, max_seqlen, scale)
     o, lse = fa_decode_paged(q, kpages, vpages, block_table, seqlens, max_seqlen, scale)
 """
@@ -33,6 +34,7 @@ _Z = ctypes.c_size_t
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_split_keys": (_I, [_I, _I, _I, _I]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
@@ -144,6 +146,39 @@ def fa_fwd_f32(q, k, v, scale=None, causal=False, out=None, lse=None, stream=Non
 
 def fa_decode_split_keys(B, H, d, max_seqlen) -> int:
     return int(load().fa_decode_split_keys(B, H, d, max_seqlen))
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None, causal=False,
+                  out=None, lse=None, stream=None):
+    """Packed variable-length forward: q [total_q,H,d], k/v [total_k,H,d] bf16,
+    cu_seqlens_q/k int32 [B+1] on the device, max_seqlen_q a host int >= every
+    query count.  Returns (O bf16 [total_q,H,d], LSE fp32 [H,total_q])."""
+    import torch
+
+    lib = load()
+    pq = _dev(q, "q", torch.bfloat16, 3)
+    pk = _dev(k, "k", torch.bfloat16, 3)
+    pv = _dev(v, "v", torch.bfloat16, 3)
+    pcq = _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    pck = _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    Tq, H, d = q.shape
+    if k.shape[1:] != (H, d) or v.shape != k.shape:
+        raise ValueError("q, k, v shapes disagree")
+    if cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B+1 entries")
+    B = cu_seqlens_q.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    po = _dev(out, "out", torch.bfloat16, 3)
+    pl = _dev(lse, "lse", torch.float32, 2)
+    st = lib.fa_fwd_varlen(pq, pk, pv, po, pl, pcq, pck, B, H, d, Tq, int(max_seqlen_q),
+                           float(scale), 1 if causal else 0, _stream(q, stream))
+    _check(st, "fa_fwd_varlen")
+    return out, lse
 
 
 def fa_decode_workspace_bytes(B, H, d, max_seqlen, split_keys=0) -> int:

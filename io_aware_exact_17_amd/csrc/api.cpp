@@ -85,6 +85,27 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
   return fwd_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, stream, true);
 }
 
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int H, int d,
+                  int total_q, int max_seqlen_q, float scale, int causal, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse) ||
+      !aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k))
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || B > kMaxGridYZ || H < 1 || total_q < 1 || max_seqlen_q < 1) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H > INT_MAX) return FA_ERR_INVALID_ARG;
+  if (max_seqlen_q > total_q) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // grid = (query tiles of the longest sequence x H, B), same tile height as dense
+  if (fa::fwd_bf16_grid(1, H, max_seqlen_q) > kMaxGridX) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, max_seqlen_q, 0, d, scale, causal ? 1 : 0, stream};
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_decode_split_keys(int B, int H, int d, int max_seqlen) {
   (void)d;
   if (B < 1 || H < 1 || max_seqlen < 1) return 0;

@@ -188,11 +188,17 @@ struct QuarterOps {
   bf16x8 v[D / 64];  // V^T operands of dim blocks (q'%2)*NDB/2 + i
 };
 
-template <int D, bool CAUSAL>
+// VARLEN: a packed batch of sequences of different lengths, token-major
+// ([T, H, d], rows of one head H*d elements apart), sequence b owning query
+// rows cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1, LSE
+// [H, total_q]; grid (the longest sequence's query tiles x H, B).
+// Otherwise [B, H, N, d] with contiguous rows per head.
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int Nq, int Nk,
-    float c, int n_qtiles) {
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int Nq_dense, int Nk_dense,
+    float c, int n_qtiles, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    int H, int total_q) {
   using C = FwdCfg<D>;
   using Ops = QuarterOps<D>;
   constexpr int TB = C::TILE * 2;        // bytes per K or V tile
@@ -210,12 +216,36 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group this lane holds
 
   // Heaviest query tile first; heads vary fastest.
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH);
+  int qt, Nq, Nk;
+  size_t qbase, kbase, lse_base;  // elements
+  if constexpr (VARLEN) {
+    // One sequence after another (grid.y), so the workgroups running
+    // together share that sequence's K/V in L2; within it, heaviest tile
+    // first, heads fastest.
+    const int h = (int)(blockIdx.x % H);
+    const int b = (int)blockIdx.y;
+    qt = n_qtiles - 1 - (int)(blockIdx.x / H);
+    const int qs = cu_q[b], ks = cu_k[b];
+    Nq = cu_q[b + 1] - qs;
+    Nk = cu_k[b + 1] - ks;
+    if (qt * kBR >= Nq) return;  // past this sequence's last query tile
+    qbase = ((size_t)qs * H + h) * D;
+    kbase = ((size_t)ks * H + h) * D;
+    lse_base = (size_t)h * total_q + qs;
+  } else {
+    qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
+    const int bh = (int)(blockIdx.x % BH);
+    Nq = Nq_dense;
+    Nk = Nk_dense;
+    qbase = (size_t)bh * Nq * D;
+    kbase = (size_t)bh * Nk * D;
+    lse_base = (size_t)bh * Nq;
+  }
+  // Row strides in global memory (a head's rows are contiguous when dense).
+  const size_t q_rs = VARLEN ? (size_t)H * D : (size_t)D;       // elements
+  const uint32_t kv_rsb = VARLEN ? (uint32_t)(H * ROWB) : ROWB;  // bytes
   const int q0 = qt * kBR;
   const int off = Nk - Nq;  // bottom-right causal alignment
-  const size_t qbase = (size_t)bh * Nq * D;
-  const size_t kbase = (size_t)bh * Nk * D;
 
   const int kv_end = CAUSAL ? min(Nk, q0 + kBR + off) : Nk;
   const int n_tiles = kv_end > 0 ? (kv_end + kBC - 1) / kBC : 0;
@@ -234,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   bf16x8 qf[2][C::KS];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const bf16* src = Q + qbase + (size_t)min(qi0 + 32 * rb, Nq - 1) * D + 8 * half;
+    const bf16* src = Q + qbase + (size_t)min(qi0 + 32 * rb, Nq - 1) * q_rs + 8 * half;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) qf[rb][s] = load_to_acc(src + 16 * s);
   }
@@ -252,13 +282,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < C::IPW; ++i) {
     const int r = (wave * C::IPW + i) * C::RPI + ld_row;
-    g_off[i] = (uint32_t)(r * ROWB + swz<D>(r, ld_slot) * 16);  // the permutation is its own inverse
+    g_off[i] = (uint32_t)(r * kv_rsb + swz<D>(r, ld_slot) * 16);  // the permutation is its own inverse
   }
   const char* const kg = reinterpret_cast<const char*>(K + kbase);
   const char* const vg = reinterpret_cast<const char*>(V + kbase);
   const uint32_t lds_wave = (uint32_t)(size_t)lds + wave * C::IPW * 1024;
   auto issue = [&](const char* base, int region, int j) {
-    const char* t = base + (size_t)j * TB;
+    const char* t = base + (size_t)j * kBC * kv_rsb;
     uint32_t dst = lds_wave;
     asm volatile("" : "+s"(dst));
     dst += region;
@@ -270,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i) {
         const int r = (wave * C::IPW + i) * C::RPI + ld_row;
-        copy_to_lds(t, (uint32_t)(min(r, last) * ROWB + swz<D>(r, ld_slot) * 16), dst + i * 1024);
+        copy_to_lds(t, (uint32_t)(min(r, last) * kv_rsb + swz<D>(r, ld_slot) * 16), dst + i * 1024);
       }
     }
   };
@@ -720,7 +750,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       }
     const int row = qi0 + 32 * rb;
     if (half == 0 && row < Nq)
-      LSE[(size_t)bh * Nq + row] = l_tot > 0.f ? (m_ref[rb] + log2_hw(l_tot)) * kLn2 : kNegInf;
+      LSE[lse_base + row] = l_tot > 0.f ? (m_ref[rb] + log2_hw(l_tot)) * kLn2 : kNegInf;
   }
   // Same wave wrote the region, so program order is enough between the
   // writes and these reads.
@@ -731,30 +761,33 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const int c = lane % C::CPR;
     const u32x4 w = *reinterpret_cast<const lds_u32x4*>(otile + r * ROWB + ((c ^ (r & 15)) * 16));
     const int row = wq0 + r;
-    if (row < Nq) *reinterpret_cast<u32x4*>(O + qbase + (size_t)row * D + c * 8) = w;
+    if (row < Nq) *reinterpret_cast<u32x4*>(O + qbase + (size_t)row * q_rs + c * 8) = w;
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdArgs& a) {
   const int n_qtiles = (a.Nq + kBR - 1) / kBR;
   const int BH = a.B * a.H;
   // Scores enter the exponent as s * c (log2 units); masking acts on P,
   // so c may have either sign or be zero.
   const float c = a.scale * kLog2e;
-  const dim3 grid((unsigned)(n_qtiles * BH));
+  const dim3 grid = VARLEN ? dim3((unsigned)(n_qtiles * a.H), (unsigned)a.B)
+                           : dim3((unsigned)(n_qtiles * BH));
   const dim3 block(kThreads);
-  void* args[] = {(void*)&a.q, (void*)&a.k, (void*)&a.v, (void*)&a.o, (void*)&a.lse,
-                  (void*)&BH, (void*)&a.Nq, (void*)&a.Nk, (void*)&c, (void*)&n_qtiles};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL>), grid, block,
-                         args, 0, a.stream);
+  void* args[] = {(void*)&a.q,    (void*)&a.k,    (void*)&a.v,  (void*)&a.o,       (void*)&a.lse,
+                  (void*)&BH,     (void*)&a.Nq,   (void*)&a.Nk, (void*)&c,         (void*)&n_qtiles,
+                  (void*)&a.cu_q, (void*)&a.cu_k, (void*)&a.H,  (void*)&a.total_q};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL, VARLEN>), grid,
+                         block, args, 0, a.stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch<128, true>(a) : launch<128, false>(a);
-  return launch_fwd_bf16_d64(a);
+  if (a.d != 128) return launch_fwd_bf16_d64(a);
+  if (a.cu_q) return a.causal ? launch<128, true, true>(a) : launch<128, false, true>(a);
+  return a.causal ? launch<128, true, false>(a) : launch<128, false, false>(a);
 }
 
 long long fwd_bf16_grid(int B, int H, int Nq) {

@@ -88,11 +88,16 @@ __device__ __forceinline__ int vt_pos4(int group4) {
   return ((group4 & 1) << 1) | ((group4 >> 1) & 1);
 }
 
-template <int D, bool CAUSAL>
+// VARLEN: a packed batch of sequences (token-major [T, H, d], sequence b owns
+// query rows cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1, LSE
+// [H, total_q], grid (the longest sequence's query tiles x H, B)); otherwise
+// dense [B, H, N, d].
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int Nq, int Nk,
-    float c, int negate_q, int n_qtiles) {
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int Nq_dense, int Nk_dense,
+    float c, int negate_q, int n_qtiles, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, int H, int total_q) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
   __shared__ __attribute__((aligned(16))) bf16 smem[C::LDS_ELEMS];
@@ -107,12 +112,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group this lane holds
 
   // Heaviest query tile first; heads vary fastest.
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH);
+  int qt, Nq, Nk;
+  size_t qbase, kbase, lse_base;  // elements
+  if constexpr (VARLEN) {
+    // One sequence after another (grid.y), so the workgroups running
+    // together share that sequence's K/V in L2; within it, heaviest tile
+    // first, heads fastest.
+    const int h = (int)(blockIdx.x % H);
+    const int b = (int)blockIdx.y;
+    qt = n_qtiles - 1 - (int)(blockIdx.x / H);
+    const int qs = cu_q[b], ks = cu_k[b];
+    Nq = cu_q[b + 1] - qs;
+    Nk = cu_k[b + 1] - ks;
+    if (qt * kBR >= Nq) return;  // past this sequence's last query tile
+    qbase = ((size_t)qs * H + h) * D;
+    kbase = ((size_t)ks * H + h) * D;
+    lse_base = (size_t)h * total_q + qs;
+  } else {
+    qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
+    const int bh = (int)(blockIdx.x % BH);
+    Nq = Nq_dense;
+    Nk = Nk_dense;
+    qbase = (size_t)bh * Nq * D;
+    kbase = (size_t)bh * Nk * D;
+    lse_base = (size_t)bh * Nq;
+  }
+  const int rs = VARLEN ? H * D : D;  // elements between consecutive rows of a head
   const int q0 = qt * kBR;
   const int off = Nk - Nq;  // bottom-right causal alignment
-  const size_t qbase = (size_t)bh * Nq * D;
-  const size_t kbase = (size_t)bh * Nk * D;
 
   const int kv_end = CAUSAL ? min(Nk, q0 + kBR + off) : Nk;
   const int n_tiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
@@ -127,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   bf16x8 qf[C::KS];
   {
     const uint32_t flip = negate_q ? 0x80008000u : 0u;  // exact sign flip for a negative scale
-    const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)min(qi, Nq - 1) * D);
+    const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)min(qi, Nq - 1) * rs);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       u32x4 w = src[2 * s + half];
@@ -157,12 +184,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // scores are masked to -inf, so they carry zero weight.
   auto load_tile = [&](int j) {
     const int k0 = j * BC;
-    const char* base = reinterpret_cast<const char*>((k_mover ? K : V) + kbase + (size_t)k0 * D);
+    const char* base = reinterpret_cast<const char*>((k_mover ? K : V) + kbase + (size_t)k0 * rs);
     const int last = Nk - 1 - k0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = min(first_key + key_step * i, last);
-      stg[i] = *reinterpret_cast<const u32x4*>(base + (uint32_t)((key * D + dcol) * 2));
+      stg[i] = *reinterpret_cast<const u32x4*>(base + (uint32_t)((key * rs + dcol) * 2));
     }
   };
   auto store_tile = [&](int j) {
@@ -337,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const float l_tot = sum_across_halves(l_part);
   if (qi < Nq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16* orow = O + qbase + (size_t)qi * D;
+    bf16* orow = O + qbase + (size_t)qi * rs;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -347,11 +374,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * half) = w;
       }
     if (half == 0)
-      LSE[(size_t)bh * Nq + qi] = l_tot > 0.f ? (m_ref + log2_hw(l_tot)) * kLn2 : kNegInf;
+      LSE[lse_base + qi] = l_tot > 0.f ? (m_ref + log2_hw(l_tot)) * kLn2 : kNegInf;
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdArgs& a) {
   const int n_qtiles = (a.Nq + kBR - 1) / kBR;
   const int BH = a.B * a.H;
@@ -360,19 +387,22 @@ hipError_t launch(const FwdArgs& a) {
   // against the reference, so the weights are exactly uniform, as for 0.
   const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   const int neg = a.scale < 0.f ? 1 : 0;
-  const dim3 grid((unsigned)(n_qtiles * BH));
+  const dim3 grid = VARLEN ? dim3((unsigned)(n_qtiles * a.H), (unsigned)a.B)
+                           : dim3((unsigned)(n_qtiles * BH));
   const dim3 block(kThreads);
-  void* args[] = {(void*)&a.q, (void*)&a.k, (void*)&a.v, (void*)&a.o, (void*)&a.lse,
-                  (void*)&BH, (void*)&a.Nq, (void*)&a.Nk, (void*)&c, (void*)&neg,
-                  (void*)&n_qtiles};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL>), grid, block,
-                         args, 0, a.stream);
+  void* args[] = {(void*)&a.q,    (void*)&a.k,        (void*)&a.v,    (void*)&a.o,
+                  (void*)&a.lse,  (void*)&BH,         (void*)&a.Nq,   (void*)&a.Nk,
+                  (void*)&c,      (void*)&neg,        (void*)&n_qtiles, (void*)&a.cu_q,
+                  (void*)&a.cu_k, (void*)&a.H,        (void*)&a.total_q};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL, VARLEN>), grid,
+                         block, args, 0, a.stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16_d64(const FwdArgs& a) {
-  return a.causal ? launch<64, true>(a) : launch<64, false>(a);
+  if (a.cu_q) return a.causal ? launch<64, true, true>(a) : launch<64, false, true>(a);
+  return a.causal ? launch<64, true, false>(a) : launch<64, false, false>(a);
 }
 
 }  // namespace fa

@@ -18,6 +18,13 @@ struct FwdArgs {
   float scale;
   int causal;
   hipStream_t stream;
+  // Packed variable-length batch (null for the dense [B, H, N, d] layout):
+  // q, o [total_q, H, d], k, v [total_k, H, d], lse [H, total_q]; sequence b
+  // owns query rows cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1;
+  // Nq is then the longest query length (it sizes the grid).
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_k = nullptr;
+  int total_q = 0;
 };
 
 struct DecodeArgs {

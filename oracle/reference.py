@@ -184,3 +184,33 @@ def decode_paged(q, kpages, vpages, block_table, seqlens, scale, heads=None, seq
             L[b, h] = lse[0]
     return O, L
 
+
+def attention_varlen(q, k, v, cu_q, cu_k, scale, causal=False, seqs=None, heads=None):
+    """Exact attention over a packed batch of sequences of different lengths.
+
+    q: [Tq, H, d], k: [Tk, H, d], v: [Tk, H, dv], token-major; sequence b owns
+    query rows cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1, and
+    attends only within itself.  Causal masking is bottom-right aligned within
+    each sequence (its queries are the last of its keys, as in a chunked
+    prefill).  `seqs` / `heads` restrict the evaluation (others stay NaN).
+
+    Returns O [Tq, H, dv] and LSE [H, Tq], float64."""
+    cu_q = [int(x) for x in (cu_q.cpu() if hasattr(cu_q, "cpu") else cu_q)]
+    cu_k = [int(x) for x in (cu_k.cpu() if hasattr(cu_k, "cpu") else cu_k)]
+    Tq, H, _ = q.shape
+    dv = v.shape[-1]
+    O = np.full((Tq, H, dv), np.nan)
+    L = np.full((H, Tq), np.nan)
+    seqs = range(len(cu_q) - 1) if seqs is None else seqs
+    heads = range(H) if heads is None else heads
+    for b in seqs:
+        qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if qe == qs:
+            continue
+        for h in heads:
+            o, lse = head_attention(_f64(q[qs:qe, h]), _f64(k[ks:ke, h]), _f64(v[ks:ke, h]),
+                                    scale, causal)
+            O[qs:qe, h] = o
+            L[h, qs:qe] = lse
+    return O, L
+

@@ -245,6 +245,62 @@ def test_decode_workspace_reused_across_calls(fa):
         check(o, lse, O, L, TOL_BF16, f"reuse call {call}")
 
 
+VARLEN_CASES = [
+    # (d, causal, query lengths, key lengths)
+    (128, True, [1, 255, 256, 257, 600, 0, 1000], [1, 255, 256, 257, 600, 0, 1000]),
+    (128, True, [100, 300, 1], [900, 300, 4000]),     # chunked prefill: keys before the queries
+    (128, True, [300, 70], [64, 0]),                  # more queries than keys: empty rows
+    (128, False, [513, 7, 64], [1025, 33, 64]),
+    (64, True, [1, 129, 500], [1, 700, 500]),
+    (64, False, [200, 40], [77, 3000]),
+]
+
+
+@pytest.mark.parametrize("d,causal,lq,lk", VARLEN_CASES)
+def test_fwd_varlen(fa, d, causal, lq, lk):
+    log(f"case varlen d={d} causal={causal} lq={lq} lk={lk}")
+    H = 3
+    q, k, v, cq, ck = W.varlen_inputs(lq, lk, H, d, seed=61 + d + len(lq), device="cuda")
+    o, lse = fa.fa_fwd_varlen(q, k, v, cq, ck, max(lq), 1 / math.sqrt(d), causal)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_varlen(q, k, v, cq, ck, 1 / math.sqrt(d), causal)
+    check(o, lse, O, L, TOL_BF16, "varlen")
+
+
+@pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, True)])
+def test_fwd_varlen_equals_dense(fa, d, causal):
+    """Sequences of one length packed token-major give exactly the dense
+    kernel's result on the [B, H, N, d] layout (same tiles, same arithmetic)."""
+    log(f"case varlen vs dense d={d} causal={causal}")
+    B, H, N = 3, 4, 700
+    q, k, v = W.prefill_inputs(B, H, N, N, d, "bf16", seed=71, device="cuda")
+    o, lse = fa.fa_fwd(q, k, v, 0.09, causal)
+    pack = lambda t: t.permute(0, 2, 1, 3).reshape(B * N, H, d).contiguous()  # noqa: E731
+    cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device="cuda")
+    o2, lse2 = fa.fa_fwd_varlen(pack(q), pack(k), pack(v), cu, cu, N, 0.09, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(pack(o), o2)
+    assert torch.equal(lse.permute(1, 0, 2).reshape(H, B * N), lse2)
+
+
+def test_fwd_varlen_full_size_sampled(fa):
+    """The packed causal workload (8 sequences, lengths U[512, 8192], H=32):
+    shortest and longest sequence, two heads each, against the oracle."""
+    s = W.VARLEN_PREFILL
+    lens, q, k, v, cq, ck = W.varlen_spec_inputs(s, "cuda")
+    log(f"case {s.name} lens={lens.tolist()}")
+    o, lse = fa.fa_fwd_varlen(q, k, v, cq, ck, int(lens.max()), s.scale, s.causal)
+    torch.cuda.synchronize()
+    seqs = [int(torch.argmin(lens)), int(torch.argmax(lens))]
+    heads = [0, s.H - 1]
+    O, L = oracle.attention_varlen(q, k, v, cq, ck, s.scale, s.causal, seqs=seqs, heads=heads)
+    cqh = cq.cpu().tolist()
+    for b in seqs:
+        r = slice(cqh[b], cqh[b + 1])
+        for h in heads:
+            check(o[r, h], lse[h, r], O[r, h], L[h, r], TOL_BF16, f"seq {b} head {h}")
+
+
 def paged_copy(kc, vc, sl, off, page_size, seed, spare=3, max_len=None):
     bt, npg = W.paged_layout(sl, page_size, seed=seed, spare_pages=spare, max_len=max_len)
     kp = W.to_pages(kc, sl, off, bt, page_size, npg)

@@ -346,3 +346,33 @@ def test_paged_decode_oracle_is_packed_decode(P):
     bad[b, 0] = bt[other, 0]
     O3, _ = oracle.decode_paged(q, kp, vp, bad, lens, 0.3)
     assert not np.allclose(O3[b], O1[b])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_oracle_against_brute_force(causal):
+    """Packed sequences of different lengths (an empty one, queries fewer than
+    keys as in a chunked prefill): every sequence attends only within itself,
+    bottom-right aligned; checked against the pure-Python definition run per
+    sequence."""
+    rng = np.random.default_rng(5)
+    lq, lk = [3, 0, 5, 1, 4], [3, 2, 9, 4, 0]
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(lk)])
+    H, d = 2, 4
+    q = rng.standard_normal((cq[-1], H, d))
+    k = rng.standard_normal((ck[-1], H, d))
+    v = rng.standard_normal((ck[-1], H, 3))
+    O, L = oracle.attention_varlen(q, k, v, cq, ck, 0.7, causal)
+    for b in range(len(lq)):
+        qb = [[q[cq[b]:cq[b + 1], h].tolist() for h in range(H)]]
+        kb = [[k[ck[b]:ck[b + 1], h].tolist() for h in range(H)]]
+        vb = [[v[ck[b]:ck[b + 1], h].tolist() for h in range(H)]]
+        Ob, Lb = brute.attention(qb, kb, vb, 0.7, causal)
+        for h in range(H):
+            for i in range(lq[b]):
+                r = cq[b] + i
+                if lk[b] == 0 or (causal and i + lk[b] - lq[b] < 0):
+                    assert np.all(O[r, h] == 0) and L[h, r] == -np.inf
+                    continue
+                close(O[r, h], np.array(Ob[0][h][i]), 1e-13)
+                close(L[h, r], Lb[0][h][i], 1e-13)

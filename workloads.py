@@ -80,6 +80,33 @@ DECODE_BATCHED = DecodeSpec("decode_batched_b64_h32_len128-16384_d128", 64, 32, 
 LONG_PREFILL = PrefillSpec("prefill_causal_h32_n8192_d128", 1, 32, 8192, 8192, 128, "bf16", True, 1705)
 
 
+@dataclass(frozen=True)
+class VarlenSpec:
+    name: str
+    B: int
+    H: int
+    d: int
+    min_len: int
+    max_len: int
+    seed: int
+    causal: bool
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self, lens) -> float:
+        """4*H*d*Lq*Lk per sequence, halved when causal (the dense convention)."""
+        tot = sum(int(x) * int(x) for x in lens)
+        return 4.0 * self.H * self.d * tot / (2.0 if self.causal else 1.0)
+
+
+# Packed variable-length causal prefill: 8 sequences, lengths uniform in
+# [512, 8192] (queries = keys per sequence).
+VARLEN_PREFILL = VarlenSpec("prefill_varlen_b8_h32_len512-8192_d128_causal", 8, 32, 128, 512, 8192,
+                            1706, True)
+
+
 def _gen(device, seed: int) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(seed)
@@ -179,6 +206,31 @@ def to_pages(cache, seqlens, offsets, block_table, page_size, num_pages):
     if src:
         pool[torch.cat(dst).to(dev)] = cache[torch.cat(src).to(dev)]
     return pool.view(num_pages, page_size, H, d)
+
+
+def varlen_inputs(lens_q, lens_k, H, d, seed=0, device="cpu", dtype="bf16"):
+    """Packed token-major batch: q [sum Lq, H, d], k, v [sum Lk, H, d] N(0,1),
+    and int32 cu_seqlens_q / cu_seqlens_k [B+1] (exclusive prefix sums with the
+    total appended), all on `device`."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    lq = torch.as_tensor(lens_q, dtype=torch.int64).cpu()
+    lk = torch.as_tensor(lens_k, dtype=torch.int64).cpu()
+    cq = torch.zeros(len(lq) + 1, dtype=torch.int64)
+    ck = torch.zeros(len(lk) + 1, dtype=torch.int64)
+    cq[1:] = torch.cumsum(lq, 0)
+    ck[1:] = torch.cumsum(lk, 0)
+    g = _gen(device, seed + 7919)
+    Tq, Tk = int(cq[-1]), int(ck[-1])
+    q = _normal((max(Tq, 1), H, d), g, device, tdt)[:Tq].contiguous()
+    k = _normal((max(Tk, 1), H, d), g, device, tdt)[:Tk].contiguous()
+    v = _normal((max(Tk, 1), H, d), g, device, tdt)[:Tk].contiguous()
+    return q, k, v, cq.to(torch.int32).to(device), ck.to(torch.int32).to(device)
+
+
+def varlen_spec_inputs(spec: VarlenSpec, device="cpu"):
+    """The spec's lengths (drawn first, on the host) and its packed inputs."""
+    lens = decode_lengths(spec.B, spec.min_len, spec.max_len, spec.seed)
+    return (lens,) + varlen_inputs(lens, lens, spec.H, spec.d, spec.seed, device)
 
 
 def decode_kv_bytes(seqlens, H, d, elem_bytes=2) -> int:
