@@ -214,3 +214,54 @@ def attention_varlen(q, k, v, cu_q, cu_k, scale, causal=False, seqs=None, heads=
             L[h, qs:qe] = lse
     return O, L
 
+
+def head_attention_grad(Q, K, V, dO, scale, causal=False):
+    """Gradients of exact attention for one head, from the definition.
+
+    With S = scale * Q K^T (hidden keys masked), P = softmax(S) row-wise and
+    O = P V, the chain rule through O and through the row softmax gives
+
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - rowsum(P * dP))      (the softmax Jacobian, row by row)
+        dQ = scale * dS K,   dK = scale * dS^T Q
+
+    all materialised in float64.  A row with no visible key has P = 0 and
+    contributes nothing.  The pages keep only O and the row statistics and
+    recompute the needed blocks in the backward pass (AI圣经13 review §03,
+    "recomputation"; explainer §3); this is the plain definition that such a
+    backward must reproduce.
+
+    Returns (dQ [n, d], dK [Nk, d], dV [Nk, dv]) float64."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    n, Nk = Q.shape[0], K.shape[0]
+    S = f32_scale(scale) * (Q @ K.T)
+    if causal:
+        hidden = np.arange(Nk)[None, :] > (np.arange(n) + (Nk - n))[:, None]
+        S = np.where(hidden, NEG_INF, S)
+    m = S.max(axis=1) if Nk > 0 else np.full(n, NEG_INF)
+    empty = m == NEG_INF
+    E = np.exp(S - np.where(empty, 0.0, m)[:, None])
+    P = E / np.where(empty, 1.0, E.sum(axis=1))[:, None]
+    P[empty] = 0.0
+    dV = P.T @ dO
+    dP = dO @ V.T
+    dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+    sc = f32_scale(scale)
+    return sc * (dS @ K), sc * (dS.T @ Q), dV
+
+
+def attention_grad(q, k, v, do, scale, causal=False, heads=None):
+    """head_attention_grad over [B, H, N, d] tensors; returns dQ, dK, dV
+    (float64, same shapes as q, k, v).  `heads`: optional list of (b, h)
+    pairs to evaluate (others stay NaN)."""
+    B, H = q.shape[0], q.shape[1]
+    dQ = np.full(q.shape, np.nan)
+    dK = np.full(k.shape, np.nan)
+    dV = np.full(v.shape, np.nan)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in pairs:
+        dQ[b, h], dK[b, h], dV[b, h] = head_attention_grad(q[b, h], k[b, h], v[b, h], do[b, h],
+                                                           scale, causal)
+    return dQ, dK, dV
+

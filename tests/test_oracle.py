@@ -376,3 +376,109 @@ def test_varlen_oracle_against_brute_force(causal):
                     continue
                 close(O[r, h], np.array(Ob[0][h][i]), 1e-13)
                 close(L[h, r], Lb[0][h][i], 1e-13)
+
+
+# ------------------------------------------------------------- backward pass
+
+def _torch_grads(Q, K, V, dO, scale, causal):
+    q, k, v = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+    S = float(np.float32(scale)) * q @ k.T
+    n, Nk = Q.shape[0], K.shape[0]
+    if causal:
+        S = S.masked_fill(torch.arange(Nk)[None, :] > (torch.arange(n) + (Nk - n))[:, None],
+                          -float("inf"))
+    P = torch.softmax(S, 1).nan_to_num(0.0)  # rows with no visible key: P = 0
+    (P @ v * torch.tensor(dO)).sum().backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+@pytest.mark.parametrize("causal,n,Nk", [(False, 6, 9), (True, 6, 9), (True, 9, 6), (False, 1, 1)])
+def test_grad_oracle_matches_float64_autograd(causal, n, Nk):
+    rng = np.random.default_rng(n * 10 + Nk)
+    Q, K = rng.standard_normal((n, 5)), rng.standard_normal((Nk, 5))
+    V, dO = rng.standard_normal((Nk, 3)), rng.standard_normal((n, 3))
+    got = oracle.head_attention_grad(Q, K, V, dO, 0.4, causal)
+    for g, t in zip(got, _torch_grads(Q, K, V, dO, 0.4, causal)):
+        close(g, t, 1e-13)
+
+
+def test_grad_oracle_matches_finite_differences():
+    """Central differences of L = sum(O * dO) through the forward oracle."""
+    rng = np.random.default_rng(3)
+    Q, K, V = rng.standard_normal((3, 2)), rng.standard_normal((4, 2)), rng.standard_normal((4, 2))
+    dO = rng.standard_normal((3, 2))
+    for causal in (False, True):
+        got = oracle.head_attention_grad(Q, K, V, dO, 0.7, causal)
+
+        def loss(Qx, Kx, Vx):
+            return float((ref.head_attention(Qx, Kx, Vx, 0.7, causal)[0] * dO).sum())
+
+        for which, X in enumerate((Q, K, V)):
+            num = np.zeros_like(X)
+            for idx in np.ndindex(X.shape):
+                args = [Q.copy(), K.copy(), V.copy()]
+                h = 1e-6
+                args[which][idx] += h
+                up = loss(*args)
+                args[which][idx] -= 2 * h
+                num[idx] = (up - loss(*args)) / (2 * h)
+            close(got[which], num, 1e-7)
+
+
+def test_grad_closed_forms():
+    rng = np.random.default_rng(4)
+    n, d = 5, 4
+    Q, dO = rng.standard_normal((n, d)), rng.standard_normal((n, 3))
+    # one key: P = 1, so dS = 0 -> dQ = dK = 0 and dV = sum of dO
+    K1, V1 = rng.standard_normal((1, d)), rng.standard_normal((1, 3))
+    dQ, dK, dV = oracle.head_attention_grad(Q, K1, V1, dO, 0.3)
+    assert np.abs(dQ).max() < 1e-15 and np.abs(dK).max() < 1e-15
+    close(dV[0], dO.sum(axis=0), 1e-14)
+    # identical keys: P uniform, each row of dS sums to zero -> dQ = 0
+    K = np.repeat(rng.standard_normal((1, d)), 6, axis=0)
+    V = rng.standard_normal((6, 3))
+    dQ, _, dV = oracle.head_attention_grad(Q, K, V, dO, 0.3)
+    assert np.abs(dQ).max() < 1e-14
+    close(dV, np.repeat(dO.sum(axis=0, keepdims=True) / 6, 6, axis=0), 1e-14)
+    # causal with more queries than keys: the first rows see no key and add nothing
+    Q2, dO2 = rng.standard_normal((7, d)), rng.standard_normal((7, 3))
+    dQ, dK, dV = oracle.head_attention_grad(Q2, K[:3], V[:3], dO2, 0.3, causal=True)
+    assert np.all(dQ[:4] == 0)
+    g2 = oracle.head_attention_grad(Q2[4:], K[:3], V[:3], dO2[4:], 0.3, causal=True)
+    close(dK, g2[1], 1e-14)
+    close(dV, g2[2], 1e-14)
+
+
+def test_grad_row_term_equals_rowsum_do_o():
+    """rowsum(P * dP) = rowsum(dO * O): the per-row term the backward can take
+    from the saved output instead of from the scores."""
+    rng = np.random.default_rng(6)
+    Q, K, V = rng.standard_normal((8, 4)), rng.standard_normal((11, 4)), rng.standard_normal((11, 4))
+    dO = rng.standard_normal((8, 4))
+    O, _ = ref.head_attention(Q, K, V, 0.5, causal=True)
+    S = float(np.float32(0.5)) * Q @ K.T
+    S = np.where(np.arange(11)[None, :] > (np.arange(8) + 3)[:, None], -np.inf, S)
+    P = np.exp(S - S.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    close((P * (dO @ V.T)).sum(1), (dO * O).sum(1), 1e-13)
+
+
+def test_grad_planted_mistakes_are_caught():
+    """Plausible slips in the gradient formulas fail the autograd pin."""
+    rng = np.random.default_rng(8)
+    Q, K, V, dO = (rng.standard_normal(s) for s in ((6, 4), (9, 4), (9, 4), (6, 4)))
+    want = _torch_grads(Q, K, V, dO, 0.4, False)
+    sc = float(np.float32(0.4))
+    S = sc * Q @ K.T
+    E = np.exp(S - S.max(1, keepdims=True))
+    P = E / E.sum(1, keepdims=True)
+    dP = dO @ V.T
+    slips = {
+        "no softmax Jacobian term": (sc * (P * dP) @ K, 0),
+        "Jacobian term summed over the wrong axis": (sc * (P * (dP - (P * dP).sum(0))) @ K, 0),
+        "dQ without the scale": ((P * (dP - (P * dP).sum(1, keepdims=True))) @ K, 0),
+        "dK with the unnormalised weights": (sc * ((E * (dP - (P * dP).sum(1, keepdims=True))).T @ Q), 1),
+        "dV with the unnormalised weights": (E.T @ dO, 2),
+    }
+    for name, (g, which) in slips.items():
+        assert not np.allclose(g, want[which], atol=1e-6), name
