@@ -11,6 +11,8 @@ One step is one pass of the whole hot path over resident synthetic inputs:
                  random order (block table per sequence)
   5. fa_fwd_varlen     packed causal prefill of 8 sequences, lengths U[512, 8192],
                  H=32, d=128 (token-major [T, H, d], cu_seqlens)
+  6. fa_bwd            backward of call 1 (its O and LSE, a seeded dO), fp32
+                 gradients, by recomputation
 The batched decode streams ~8.7 GB, far more than the 256 MB last-level
 cache, so the single-request decode that follows reads its 128 MiB of K/V
 from HBM.  Every call is bracketed by HIP events on the stream it runs on.
@@ -177,6 +179,14 @@ def main():
     vl_lse = torch.empty(VL.H, vlq.shape[0], dtype=torch.float32, device=dev)
     vl_flops = VL.flops(vl_lens)
 
+    # Backward of the long prefill: dO seeded, O and LSE from call 1.
+    bw_do = W.prefill_inputs(P.B, P.H, P.Nq, 1, P.d, "bf16", seed=P.seed + 1, device=dev)[0]
+    bw_dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    bw_dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    bw_dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    bw_ws = torch.empty(fa.fa_bwd_workspace_bytes(P.B, P.H, P.Nq), dtype=torch.uint8, device=dev)
+    bw_flops = 2.5 * P.flops()
+
     # A plain copy of known size, untimed: its HBM counters calibrate the
     # prefill kernel's FETCH_SIZE / WRITE_SIZE when this script runs under
     # rocprofv3 --pmc.
@@ -190,7 +200,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(rec):
-        e0, e1, e2, e3, e4, e5 = ev(), ev(), ev(), ev(), ev(), ev()
+        e0, e1, e2, e3, e4, e5, e6 = ev(), ev(), ev(), ev(), ev(), ev(), ev()
         e0.record(stream)
         fa.fa_fwd(q, k, v, P.scale, True, out=o, lse=lse)
         e1.record(stream)
@@ -206,8 +216,11 @@ def main():
         fa.fa_fwd_varlen(vlq, vlk, vlv, vlcq, vlck, vl_max, VL.scale, VL.causal, out=vl_out,
                          lse=vl_lse)
         e5.record(stream)
+        fa.fa_bwd(q, k, v, o, bw_do, lse, P.scale, True, dq=bw_dq, dk=bw_dk, dv=bw_dv,
+                  workspace=bw_ws)
+        e6.record(stream)
         if rec is not None:
-            rec.append((e0, e1, e2, e3, e4, e5))
+            rec.append((e0, e1, e2, e3, e4, e5, e6))
 
     for _ in range(args.warmup):
         step(None)
@@ -226,6 +239,7 @@ def main():
     t_ds = [r[2].elapsed_time(r[3]) for r in recs]
     t_pg = [r[3].elapsed_time(r[4]) for r in recs]
     t_vl = [r[4].elapsed_time(r[5]) for r in recs]
+    t_bw = [r[5].elapsed_time(r[6]) for r in recs]
     ms_step = wall * 1e3 / args.steps
 
     flops = P.flops()
@@ -237,6 +251,7 @@ def main():
     ds_gbps = ds_bytes / (statistics.mean(t_ds) * 1e-3) / 1e9
     pg_gbps = db_bytes / (statistics.mean(t_pg) * 1e-3) / 1e9
     vl_tflops = vl_flops / (statistics.mean(t_vl) * 1e-3) / 1e12
+    bw_tflops = bw_flops / (statistics.mean(t_bw) * 1e-3) / 1e12
 
     ceil_small, ceil_big = read_ceiling(torch, fa, dev, stream, ds_bytes)
 
@@ -259,7 +274,8 @@ def main():
             "workload": "causal prefill B=1 H=32 N=8192 d=128 + batched varlen decode "
                         "64 seqs x 32 heads d=128 len U[128,16384] + single decode H=32 N=8192 d=128 "
                         "+ the batched decode over a paged cache (16-token pages) "
-                        "+ packed causal prefill 8 seqs x 32 heads d=128 len U[512,8192]",
+                        "+ packed causal prefill 8 seqs x 32 heads d=128 len U[512,8192] "
+                        "+ backward of the causal prefill",
             "prefill": {"B": P.B, "H": P.H, "Nq": P.Nq, "Nk": P.Nk, "d": P.d, "causal": True,
                         "seed": P.seed, "flops": flops, "ms_mean": round(pre_ms, 4),
                         "ms_median": round(statistics.median(t_pre), 4),
@@ -272,6 +288,8 @@ def main():
                               "ms_mean": round(statistics.mean(t_ds), 4)},
             "decode_paged": {"page_size": PAGE, "pages": pg_pages, "split_keys": pg_sk,
                              "kv_bytes": db_bytes, "ms_mean": round(statistics.mean(t_pg), 4)},
+            "backward": {"B": P.B, "H": P.H, "N": P.Nq, "d": P.d, "causal": True,
+                         "flops": bw_flops, "ms_mean": round(statistics.mean(t_bw), 4)},
             "prefill_varlen": {"B": VL.B, "H": VL.H, "d": VL.d, "causal": VL.causal,
                                "seed": VL.seed, "lengths": [int(x) for x in vl_lens],
                                "flops": vl_flops, "ms_mean": round(statistics.mean(t_vl), 4)},
@@ -299,6 +317,9 @@ def main():
         },
         "varlen": {"unit": "TFLOP/s", "prefill_varlen": round(vl_tflops, 2),
                    "frac_of_bf16_peak": round(vl_tflops / PEAK_BF16_TFLOPS, 4)},
+        "backward": {"unit": "TFLOP/s", "value": round(bw_tflops, 2),
+                     "frac_of_bf16_peak": round(bw_tflops / PEAK_BF16_TFLOPS, 4),
+                     "flops_convention": "2.5 x forward (five products of 2*N*N*d, halved causal)"},
         "cpu_baseline": cpu,
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "torch": torch.__version__,

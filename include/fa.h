@@ -92,6 +92,31 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                hipStream_t stream);
 
 /*
+ * Backward pass by recomputation (review §03: the forward keeps only O and the
+ * row statistics; the backward rebuilds the score and probability blocks on
+ * chip).  Gradients of L with respect to q, k, v for a given dL/dO, for the
+ * same attention fa_fwd computes (same scale, same causal alignment).
+ *
+ *   q, k, v, o, dout  bf16 [B, H, N, d]   (device); o and lse from fa_fwd
+ *   lse               fp32 [B, H, Nq]     (device)
+ *   dq                fp32 [B, H, Nq, d]  written (device)
+ *   dk, dv            fp32 [B, H, Nk, d]  written (device)
+ *   workspace         device scratch of at least fa_bwd_workspace_bytes(B, H,
+ *                     Nq) bytes (the row terms of the pass), owned by the
+ *                     caller, no initialisation needed; calls that run at the
+ *                     same time must not share it
+ *   d                 64 or 128
+ *
+ * Alignment as for fa_fwd (dq, dk, dv 16-byte aligned); errors as for fa_fwd,
+ * plus FA_ERR_WORKSPACE.  Three kernels are enqueued on `stream`.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, float* dq, float* dk, float* dv,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Forward over a packed batch of sequences of different lengths (variable
  * length / padding-free prefill; the pages list padding masks among the
  * semantics to get right).  Every sequence attends only within itself; with

@@ -9,6 +9,7 @@ exception is raised.
     o, lse = fa_fwd(q, k, v, scale, causal)            # bf16 [B,H,N,d]
     o, lse = fa_fwd_f32(q, k, v, scale, causal)        # fp32 [B,H,N,d]
     o, lse = fa_fwd_varlen(q, k, v, cu_q, cu_k, max_q, scale, causal)  # packed [T,H,d]
+    dq, dk, dv = fa_bwd(q, k, v, o, dout, lse, scale, causal)          # fp32 gradients
     o, lse = fa_decode_varlen(q, kcache, vcache, seqlens, offsets, max_seqlen, scale)
     o, lse = fa_decode_paged(q, kpages, vpages, block_table, seqlens, max_seqlen, scale)
 """
@@ -34,6 +35,8 @@ _Z = ctypes.c_size_t
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_split_keys": (_I, [_I, _I, _I, _I]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
@@ -146,6 +149,42 @@ def fa_fwd_f32(q, k, v, scale=None, causal=False, out=None, lse=None, stream=Non
 
 def fa_decode_split_keys(B, H, d, max_seqlen) -> int:
     return int(load().fa_decode_split_keys(B, H, d, max_seqlen))
+
+
+def fa_bwd_workspace_bytes(B, H, Nq) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, H, Nq))
+
+
+def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
+           workspace=None, stream=None):
+    """Backward of fa_fwd: q, k, v, o, dout bf16 [B,H,N,d] and lse fp32 [B,H,Nq]
+    (o and lse from the forward).  Returns (dq, dk, dv) fp32."""
+    import torch
+
+    lib = load()
+    ptrs = [_dev(t, n, torch.bfloat16, 4) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"),
+                                                       (dout, "dout"))]
+    pl = _dev(lse, "lse", torch.float32, 3)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, k, v, o, dout shapes disagree")
+    if tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("lse must be [B, H, Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    gp = [_dev(t, n, torch.float32, 4) for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_bytes(B, H, Nq), 16), dtype=torch.uint8,
+                                device=q.device)
+    pw = _dev(workspace, "workspace", torch.uint8, 1)
+    st = lib.fa_bwd(*ptrs, pl, *gp, B, H, Nq, Nk, d, float(scale), 1 if causal else 0, pw,
+                    workspace.numel(), _stream(q, stream))
+    _check(st, "fa_bwd")
+    return dq, dk, dv
 
 
 def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None, causal=False,

@@ -106,6 +106,31 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq) {
+  if (B < 1 || H < 1 || Nq < 1) return 0;
+  return 2 * (size_t)B * (size_t)H * (size_t)Nq * sizeof(float);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, float* dq, float* dk, float* dv, int B, int H, int Nq, int Nk, int d,
+           float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned4(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_INVALID_ARG;
+  if (!dims_ok(B, H, Nq, Nk)) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (fa::bwd_bf16_grid(B, H, Nq) > kMaxGridX || fa::bwd_bf16_grid(B, H, Nk) > kMaxGridX)
+    return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * Nq > (long long)kMaxGridX * 16) return FA_ERR_INVALID_ARG;  // row pass grid
+  const size_t need = fa_bwd_workspace_bytes(B, H, Nq);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace),
+                B, H, Nq, Nk, d, scale, causal ? 1 : 0, stream};
+  return fa::launch_bwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_decode_split_keys(int B, int H, int d, int max_seqlen) {
   (void)d;
   if (B < 1 || H < 1 || max_seqlen < 1) return 0;

@@ -1,0 +1,442 @@
+// bwd_bf16.hip — gradients of exact attention by recomputation (bf16 inputs,
+// fp32 gradients).
+//
+// The forward pass keeps only O and the row statistic LSE; the backward pass
+// rebuilds each block of scores and probabilities on chip from Q, K and LSE
+// instead of storing the N x N matrices (AI圣经13 review §03,
+// "recomputation"; explainer §3).  With S = scale Q K^T and P = exp(S - LSE):
+//
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = rowsum(dO * O)_i,
+//     dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Three kernels: a row pass (D, and LSE in log2 units), one with K and V
+// fixed per wave that walks the query blocks (dK, dV), one with Q and dO
+// fixed per wave that walks the key blocks (dQ).  The last two recompute S
+// and dP each (7 products per block pair instead of 5) so that no gradient
+// needs atomic accumulation across workgroups.
+//
+// Matrix-core layout (v_mfma_f32_32x32x16_bf16, wave64): lane l holds
+// A[l%32][8*(l/32) + 0..7] and B[8*(l/32) + 0..7][l%32]; accumulator register
+// r holds D[8*(r/4) + 4*(l/32) + r%4][l%32].  Products whose k index runs
+// over a block's rows (dV, dK, dQ) take P or dS straight from the
+// accumulators as the B operand and read the A operand from LDS with the
+// transposing read ds_read_b64_tr_b16, addressed so that the k order matches
+// the rows those accumulator registers hold.
+#include "cdna4.hpp"
+#include "kernels.hpp"
+
+namespace fa {
+
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kRows = 32;                  // rows of a fixed block per wave, and of a moving block
+constexpr int kFixed = kWaves * kRows;     // fixed rows per workgroup
+
+// LDS slot of 16-byte chunk c of tile row r (the forward's permutation):
+// a chunk read across 32 rows and the transposing reads are conflict-free.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (D == 128) {
+    return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  } else {
+    return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+}
+
+template <int D>
+struct Tile {
+  static constexpr int ROWB = D * 2;           // bytes per row
+  static constexpr int BYTES = kRows * ROWB;   // one 32-row tile
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int PER_THREAD = kRows * CPR / kThreads;  // chunks per thread per tile
+  static constexpr int KS = D / 16;            // k-steps over d
+  static constexpr int NDB = D / 32;           // 32-wide blocks of d
+};
+
+// Row-major operand of one k-step: lane holds row (lane%32), dims
+// 16 s + 8 (lane/32) .. +7.
+template <int D>
+__device__ __forceinline__ bf16x8 row_op(const lds_char* tile, int lane, int s) {
+  const int r = lane & 31, h = lane >> 5;
+  return *reinterpret_cast<const lds_bf16x8*>(tile + r * Tile<D>::ROWB + swz<D>(r, 2 * s + h) * 16);
+}
+
+// Transposed operand of dim block db and k-step t (tile rows 16t .. 16t+15):
+// lane holds dim 32 db + lane%32 of the rows 16t + {4h .. 4h+3, 8+4h .. 8+4h+3},
+// h = lane/32 -- the rows accumulator registers 8t .. 8t+7 of a 32-row block hold.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_op(const lds_char* tile, int lane, int db, int t) {
+  const int h = lane >> 5;
+  const int dim = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  u32x2 part[2];
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    const int row = 16 * t + 8 * cc + 4 * h + ((lane & 15) >> 2);
+    const lds_char* p = tile + row * Tile<D>::ROWB + swz<D>(row, dim >> 3) * 16 + (dim & 7) * 2;
+    part[cc] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
+}
+
+// Accumulator registers 8t .. 8t+7 packed to bf16 as a B operand.
+__device__ __forceinline__ bf16x8 pack_b(const float (&x)[16], int t) {
+  return __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(x[8 * t], x[8 * t + 1]),
+                                          pack_bf16x2(x[8 * t + 2], x[8 * t + 3]),
+                                          pack_bf16x2(x[8 * t + 4], x[8 * t + 5]),
+                                          pack_bf16x2(x[8 * t + 6], x[8 * t + 7])});
+}
+
+// 16 bytes of row min(row, n-1) of a [n, D] bf16 matrix, dims 16 s + 8 h ..
+template <int D>
+__device__ __forceinline__ bf16x8 load_row_op(const bf16* base, int row, int n, int lane, int s) {
+  const int h = lane >> 5;
+  return *reinterpret_cast<const bf16x8*>(base + (size_t)min(row, n - 1) * D + 16 * s + 8 * h);
+}
+
+// Stage a 32-row tile (rows r0 .. r0+31, clamped to n-1) of a [n, D] matrix:
+// fetch into registers, then write them to LDS.
+template <int D>
+struct Stager {
+  u32x4 v[Tile<D>::PER_THREAD];
+  __device__ __forceinline__ void fetch(const bf16* base, int r0, int n, int tid) {
+#pragma unroll
+    for (int i = 0; i < Tile<D>::PER_THREAD; ++i) {
+      const int c = tid + kThreads * i;
+      const int r = c / Tile<D>::CPR, ch = c % Tile<D>::CPR;
+      v[i] = *reinterpret_cast<const u32x4*>(base + (size_t)min(r0 + r, n - 1) * D + ch * 8);
+    }
+  }
+  __device__ __forceinline__ void store(lds_char* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < Tile<D>::PER_THREAD; ++i) {
+      const int c = tid + kThreads * i;
+      const int r = c / Tile<D>::CPR, ch = c % Tile<D>::CPR;
+      *reinterpret_cast<lds_u32x4*>(tile + r * Tile<D>::ROWB + swz<D>(r, ch) * 16) = v[i];
+    }
+  }
+};
+
+// ---------------------------------------------------------------- row pass
+// D_i = sum_d dO[i][d] O[i][d] (fp32), and LSE in log2 units, with rows that
+// saw no key (LSE = -inf) mapped to +inf so that every P of theirs is 0.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_rows_kernel(const bf16* __restrict__ O,
+                                                            const bf16* __restrict__ dO,
+                                                            const float* __restrict__ LSE,
+                                                            float* __restrict__ lse2,
+                                                            float* __restrict__ Dv, long long rows) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const long long row = (long long)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * D + sub * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * D + sub * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc += bf16_lo(a[i]) * bf16_lo(b[i]) + bf16_hi(a[i]) * bf16_hi(b[i]);
+  }
+  acc = D == 128 ? sum_row16(acc) : sum_row8(acc);
+  if (row < rows && sub == 0) {
+    Dv[row] = acc;
+    const float l = LSE[row];
+    lse2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+  }
+}
+
+// -------------------------------------------------------------- dK and dV
+// Workgroup: 4 waves x 32 keys; key tile kt = blockIdx.x / BH (early keys,
+// which the most queries see, first), (b, h) = blockIdx.x % BH.  The query
+// blocks stream through LDS (Q, dO, LSE2, D), double-buffered.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dv,
+    float* __restrict__ dK, float* __restrict__ dV, int BH, int Nq, int Nk, float c, float scale) {
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * (2 * T::BYTES + 2 * kRows * 4)];
+  lds_char* const lds = (lds_char*)smem;
+  auto q_tile = [&](int buf) { return lds + buf * (2 * T::BYTES + 256); };
+  auto do_tile = [&](int buf) { return q_tile(buf) + T::BYTES; };
+  auto st_tile = [&](int buf) { return q_tile(buf) + 2 * T::BYTES; };  // lse2[32], D[32]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int kt = (int)(blockIdx.x / BH), bh = (int)(blockIdx.x % BH);
+  const int off = Nk - Nq;
+  const int k0w = kt * kFixed + wave * kRows;  // this wave's first key
+  const bf16* Qh = Q + (size_t)bh * Nq * D;
+  const bf16* dOh = dO + (size_t)bh * Nq * D;
+  const float* l2h = lse2 + (size_t)bh * Nq;
+  const float* Dh = Dv + (size_t)bh * Nq;
+
+  // Query blocks that see any key of the workgroup / of this wave.
+  const int n_qb = (Nq + kRows - 1) / kRows;
+  const int qb_first = CAUSAL ? max(0, kt * kFixed - off) / kRows : 0;
+  const int qb_wave = CAUSAL ? max(0, k0w - off) / kRows : 0;
+
+  // Fixed operands: K and V rows of this wave's keys as B operands.
+  bf16x8 kf[T::KS], vf[T::KS];
+#pragma unroll
+  for (int s = 0; s < T::KS; ++s) {
+    kf[s] = load_row_op<D>(K + (size_t)bh * Nk * D, k0w + col, Nk, lane, s);
+    vf[s] = load_row_op<D>(V + (size_t)bh * Nk * D, k0w + col, Nk, lane, s);
+  }
+  f32x16 dk[T::NDB], dv[T::NDB];
+#pragma unroll
+  for (int i = 0; i < T::NDB; ++i) dk[i] = dv[i] = f32x16{};
+
+  Stager<D> sq, sd;
+  float st = 0.f;  // this thread's lse2 or D value of the next block (threads 0..63)
+  auto fetch = [&](int qb) {
+    sq.fetch(Qh, qb * kRows, Nq, tid);
+    sd.fetch(dOh, qb * kRows, Nq, tid);
+    if (tid < 2 * kRows) {
+      const int r = qb * kRows + (tid & (kRows - 1));
+      st = r < Nq ? (tid < kRows ? l2h[r] : Dh[r]) : (tid < kRows ? __builtin_huge_valf() : 0.f);
+    }
+  };
+  auto store = [&](int buf) {
+    sq.store(q_tile(buf), tid);
+    sd.store(do_tile(buf), tid);
+    if (tid < 2 * kRows) reinterpret_cast<__attribute__((address_space(3))) float*>(st_tile(buf))[tid] = st;
+  };
+
+  if (qb_first < n_qb) {
+    fetch(qb_first);
+    store(0);
+    __syncthreads();
+  }
+  for (int qb = qb_first; qb < n_qb; ++qb) {
+    const int buf = (qb - qb_first) & 1;
+    if (qb + 1 < n_qb) fetch(qb + 1);
+    if (qb >= qb_wave) {
+      const lds_char* qt = q_tile(buf);
+      const lds_char* dt = do_tile(buf);
+      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys:
+      // lane = key (column), register r = query 8(r/4) + 4 half + r%4.
+      f32x16 S = {}, dP = {};
+#pragma unroll
+      for (int s = 0; s < T::KS; ++s) {
+        S = mfma_32x32x16(row_op<D>(qt, lane, s), kf[s], S);
+        dP = mfma_32x32x16(row_op<D>(dt, lane, s), vf[s], dP);
+      }
+      const auto* stp = reinterpret_cast<const __attribute__((address_space(3))) float*>(st_tile(buf));
+      float P[16], dS[16];
+      const int key = k0w + col;
+      const bool diag = CAUSAL && k0w + kRows - 1 > qb * kRows + off;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(stp + 8 * g + 4 * half);
+        const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(stp + kRows + 8 * g + 4 * half);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          float p = exp2_hw(S[r] * c - l4[i]);
+          if (diag && key > qb * kRows + 8 * g + 4 * half + i + off) p = 0.f;
+          P[r] = p;
+          dS[r] = p * (dP[r] - d4[i]);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 queries.
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 pb = pack_b(P, t), sb = pack_b(dS, t);
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) {
+          dv[db] = mfma_32x32x16(tr_op<D>(dt, lane, db, t), pb, dv[db]);
+          dk[db] = mfma_32x32x16(tr_op<D>(qt, lane, db, t), sb, dk[db]);
+        }
+      }
+    }
+    if (qb + 1 < n_qb) {
+      // buffer buf ^ 1 was last read in the previous iteration, which every
+      // wave finished before that iteration's barrier
+      store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // dK^T / dV^T accumulators: lane = key, register r of dim block db =
+  // dim 32 db + 8(r/4) + 4 half + r%4.
+  const int key = k0w + col;
+  if (key < Nk) {
+    float* dKr = dK + ((size_t)bh * Nk + key) * D;
+    float* dVr = dV + ((size_t)bh * Nk + key) * D;
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * half;
+        *reinterpret_cast<f32x4*>(dKr + d0) =
+            f32x4{dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale, dk[db][4 * g + 2] * scale,
+                  dk[db][4 * g + 3] * scale};
+        *reinterpret_cast<f32x4*>(dVr + d0) =
+            f32x4{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+      }
+  }
+}
+
+// -------------------------------------------------------------------- dQ
+// Workgroup: 4 waves x 32 queries; query tile qt = n_qt - 1 - blockIdx.x / BH
+// (late queries, which see the most keys, first).  The key blocks stream
+// through LDS (K, V), double-buffered.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dv,
+    float* __restrict__ dQ, int BH, int Nq, int Nk, float c, float scale, int n_qt) {
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * T::BYTES];
+  lds_char* const lds = (lds_char*)smem;
+  auto k_tile = [&](int buf) { return lds + buf * 2 * T::BYTES; };
+  auto v_tile = [&](int buf) { return k_tile(buf) + T::BYTES; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int qt = n_qt - 1 - (int)(blockIdx.x / BH), bh = (int)(blockIdx.x % BH);
+  const int off = Nk - Nq;
+  const int q0w = qt * kFixed + wave * kRows;
+  const int q = q0w + col;  // this lane's query
+  const bf16* Kh = K + (size_t)bh * Nk * D;
+  const bf16* Vh = V + (size_t)bh * Nk * D;
+
+  // Key blocks any query of the workgroup / of this wave sees.
+  const int kv_end = CAUSAL ? min(Nk, min(Nq, (qt + 1) * kFixed) + off) : Nk;
+  const int n_kb = kv_end > 0 ? (kv_end + kRows - 1) / kRows : 0;
+  const int kv_end_w = CAUSAL ? min(Nk, min(Nq, q0w + kRows) + off) : Nk;
+  const int n_kb_w = kv_end_w > 0 ? (kv_end_w + kRows - 1) / kRows : 0;
+
+  bf16x8 qf[T::KS], df[T::KS];
+#pragma unroll
+  for (int s = 0; s < T::KS; ++s) {
+    qf[s] = load_row_op<D>(Q + (size_t)bh * Nq * D, q, Nq, lane, s);
+    df[s] = load_row_op<D>(dO + (size_t)bh * Nq * D, q, Nq, lane, s);
+  }
+  const float l2 = q < Nq ? lse2[(size_t)bh * Nq + q] : __builtin_huge_valf();
+  const float dq_row = q < Nq ? Dv[(size_t)bh * Nq + q] : 0.f;
+  f32x16 acc[T::NDB];
+#pragma unroll
+  for (int i = 0; i < T::NDB; ++i) acc[i] = f32x16{};
+
+  Stager<D> sk, sv;
+  if (n_kb > 0) {
+    sk.fetch(Kh, 0, Nk, tid);
+    sv.fetch(Vh, 0, Nk, tid);
+    sk.store(k_tile(0), tid);
+    sv.store(v_tile(0), tid);
+    __syncthreads();
+  }
+  for (int kb = 0; kb < n_kb; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < n_kb) {
+      sk.fetch(Kh, (kb + 1) * kRows, Nk, tid);
+      sv.fetch(Vh, (kb + 1) * kRows, Nk, tid);
+    }
+    if (kb < n_kb_w) {
+      const lds_char* kt_ = k_tile(buf);
+      const lds_char* vt = v_tile(buf);
+      // S^T = K Q^T and dP^T = V dO^T: lane = query (column), register r =
+      // key 8(r/4) + 4 half + r%4 of the block.
+      f32x16 S = {}, dP = {};
+#pragma unroll
+      for (int s = 0; s < T::KS; ++s) {
+        S = mfma_32x32x16(row_op<D>(kt_, lane, s), qf[s], S);
+        dP = mfma_32x32x16(row_op<D>(vt, lane, s), df[s], dP);
+      }
+      const int k0 = kb * kRows;
+      const bool edge = k0 + kRows > Nk || (CAUSAL && k0 + kRows - 1 > q0w + off);
+      float dS[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2_hw(S[r] * c - l2);
+        const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (edge && (key >= Nk || (CAUSAL && key > q + off))) p = 0.f;
+        dS[r] = p * (dP[r] - dq_row);
+      }
+      // dQ^T += K^T dS^T over the block's 32 keys.
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 sb = pack_b(dS, t);
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) acc[db] = mfma_32x32x16(tr_op<D>(kt_, lane, db, t), sb, acc[db]);
+      }
+    }
+    if (kb + 1 < n_kb) {
+      sk.store(k_tile(buf ^ 1), tid);  // last read in the previous iteration
+      sv.store(v_tile(buf ^ 1), tid);
+      __syncthreads();
+    }
+  }
+
+  if (q < Nq) {
+    float* dQr = dQ + ((size_t)bh * Nq + q) * D;
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * half;
+        *reinterpret_cast<f32x4*>(dQr + d0) =
+            f32x4{acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale, acc[db][4 * g + 2] * scale,
+                  acc[db][4 * g + 3] * scale};
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const BwdArgs& a) {
+  const int BH = a.B * a.H;
+  const float c = a.scale * kLog2e;
+  float* lse2 = a.ws;
+  float* Dv = a.ws + (size_t)BH * a.Nq;
+  const long long rows = (long long)BH * a.Nq;
+  {
+    const unsigned grid = (unsigned)((rows + (kThreads / (D / 8)) - 1) / (kThreads / (D / 8)));
+    void* args[] = {(void*)&a.o, (void*)&a.dout, (void*)&a.lse, (void*)&lse2, (void*)&Dv,
+                    (void*)&rows};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_rows_kernel<D>),
+                                         dim3(grid), dim3(kThreads), args, 0, a.stream);
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int n_kt = (a.Nk + kFixed - 1) / kFixed;
+    void* args[] = {(void*)&a.q,  (void*)&a.k,  (void*)&a.v,  (void*)&a.dout, (void*)&lse2,
+                    (void*)&Dv,   (void*)&a.dk, (void*)&a.dv, (void*)&BH,     (void*)&a.Nq,
+                    (void*)&a.Nk, (void*)&c,    (void*)&a.scale};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL>),
+                                         dim3((unsigned)(n_kt * BH)), dim3(kThreads), args, 0,
+                                         a.stream);
+    if (e != hipSuccess) return e;
+  }
+  const int n_qt = (a.Nq + kFixed - 1) / kFixed;
+  void* args[] = {(void*)&a.q,  (void*)&a.k,  (void*)&a.v,  (void*)&a.dout, (void*)&lse2,
+                  (void*)&Dv,   (void*)&a.dq, (void*)&BH,   (void*)&a.Nq,   (void*)&a.Nk,
+                  (void*)&c,    (void*)&a.scale, (void*)&n_qt};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<D, CAUSAL>),
+                         dim3((unsigned)(n_qt * BH)), dim3(kThreads), args, 0, a.stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a) {
+  if (a.d == 128) return a.causal ? launch<128, true>(a) : launch<128, false>(a);
+  return a.causal ? launch<64, true>(a) : launch<64, false>(a);
+}
+
+long long bwd_bf16_grid(int B, int H, int N) {
+  return (long long)((N + kFixed - 1) / kFixed) * B * H;
+}
+
+}  // namespace fa

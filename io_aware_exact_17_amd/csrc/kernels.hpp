@@ -47,6 +47,28 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
+// Backward pass: q, k, v, o, dout bf16 [B, H, N, d]; lse fp32 [B, H, Nq];
+// dq, dk, dv fp32 [B, H, N, d]; ws = 2 * B * H * Nq floats.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* ws;
+  int B, H, Nq, Nk, d;
+  float scale;
+  int causal;
+  hipStream_t stream;
+};
+
+hipError_t launch_bwd_bf16(const BwdArgs& a);
+long long bwd_bf16_grid(int B, int H, int N);
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);      // d = 128 here, d = 64 below
 hipError_t launch_fwd_bf16_d64(const FwdArgs& a);  // fwd_bf16_d64.hip
 hipError_t launch_fwd_f32(const FwdArgs& a);

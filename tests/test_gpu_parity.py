@@ -301,6 +301,56 @@ def test_fwd_varlen_full_size_sampled(fa):
             check(o[r, h], lse[h, r], O[r, h], L[h, r], TOL_BF16, f"seq {b} head {h}")
 
 
+# The gradients have no unit scale, so the bf16 tolerance applies relative to
+# the largest reference magnitude: P, dS and (through D = rowsum(dO * O)) O
+# enter the products in bf16, each with relative rounding 2^-9.
+TOL_GRAD_REL, TOL_GRAD_ABS = 2e-2, 1e-5
+
+
+def check_grads(got, want, what):
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        a = W.to_f64(a)
+        assert a.shape == b.shape, (name, a.shape, b.shape)
+        err = float(np.abs(a - b).max(initial=0.0))
+        ref = float(np.abs(b).max(initial=0.0))
+        log(f"  {what} {name}: err={err:.3e} max|ref|={ref:.3e}")
+        assert np.isfinite(a).all(), f"{what} {name}: non-finite"
+        assert err <= TOL_GRAD_REL * ref + TOL_GRAD_ABS, f"{what} {name}: {err} vs {ref}"
+
+
+BWD_SHAPES = [(1, 2, 1, 1), (2, 2, 33, 33), (1, 2, 100, 300), (1, 2, 300, 100), (1, 1, 129, 129),
+              (1, 2, 512, 512)]
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Nq,Nk", BWD_SHAPES)
+def test_bwd(fa, d, causal, B, H, Nq, Nk):
+    log(f"case bwd d={d} causal={causal} B={B} H={H} Nq={Nq} Nk={Nk}")
+    q, k, v = W.prefill_inputs(B, H, Nq, Nk, d, "bf16", seed=Nq + Nk + d, device="cuda")
+    do = W.prefill_inputs(B, H, Nq, 1, d, "bf16", seed=900 + Nq, device="cuda")[0]
+    sc = 1 / math.sqrt(d)
+    o, lse = fa.fa_fwd(q, k, v, sc, causal)
+    grads = fa.fa_bwd(q, k, v, o, do, lse, sc, causal)
+    torch.cuda.synchronize()
+    check_grads(grads, oracle.attention_grad(q, k, v, do, sc, causal), "bwd")
+
+
+def test_bwd_full_size_one_head(fa):
+    """The long causal shape (B=1, H=32, N=8192, d=128) through forward and
+    backward on the GPU; one whole head's three gradients against the oracle."""
+    s = W.LONG_PREFILL
+    log(f"case bwd {s.name}")
+    q, k, v = W.prefill_spec_inputs(s, "cuda")
+    do = W.prefill_inputs(s.B, s.H, s.Nq, 1, s.d, "bf16", seed=s.seed + 1, device="cuda")[0]
+    o, lse = fa.fa_fwd(q, k, v, s.scale, s.causal)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, s.scale, s.causal)
+    torch.cuda.synchronize()
+    h = 17
+    want = oracle.head_attention_grad(q[0, h], k[0, h], v[0, h], do[0, h], s.scale, s.causal)
+    check_grads((dq[0, h], dk[0, h], dv[0, h]), want, f"head {h}")
+
+
 def paged_copy(kc, vc, sl, off, page_size, seed, spare=3, max_len=None):
     bt, npg = W.paged_layout(sl, page_size, seed=seed, spare_pages=spare, max_len=max_len)
     kp = W.to_pages(kc, sl, off, bt, page_size, npg)
