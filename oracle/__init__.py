@@ -9,6 +9,7 @@ It shares no code with the HIP path.
              an independent cross-check of the definition
   brute      pure-Python loops for tiny shapes, another cross-check
 """
-from .reference import (attention, attention_grad, attention_rows, attention_varlen,  # noqa: F401
-                        decode, decode_paged, head_attention, head_attention_grad, f32_scale)
+from .reference import (attention, attention_block_sparse, attention_grad,  # noqa: F401
+                        attention_rows, attention_varlen, decode, decode_paged, head_attention,
+                        head_attention_grad, f32_scale)
 from . import online, brute  # noqa: F401

@@ -265,3 +265,44 @@ def attention_grad(q, k, v, do, scale, causal=False, heads=None):
                                                            scale, causal)
     return dQ, dK, dV
 
+
+BLOCK = 64  # rows and keys per block of a block-sparse mask
+
+
+def attention_block_sparse(q, k, v, block_mask, scale, causal=False, heads=None):
+    """Exact attention in which key j is visible to query i only if the block
+    mask admits the pair of 64-row / 64-key blocks (block_mask[h][i // 64]
+    [j // 64] != 0) and, with causal, j <= i + Nk - Nq.  The pages' way of
+    reaching long sequences skips whole tiles by a sparsity pattern (review
+    §05) without giving one; here the pattern is an input.
+
+    q: [B, H, Nq, d], k, v: [B, H, Nk, d]; block_mask [H, ceil(Nq/64),
+    ceil(Nk/64)], shared by the batch.  Rows with no visible key: O = 0,
+    LSE = -inf.  Returns O, LSE float64 (heads outside `heads`, a list of
+    (b, h) pairs, stay NaN)."""
+    B, H, Nq, _ = q.shape
+    Nk = k.shape[2]
+    M = np.asarray(block_mask.cpu() if hasattr(block_mask, "cpu") else block_mask) != 0
+    O = np.full((B, H, Nq, v.shape[-1]), np.nan)
+    L = np.full((B, H, Nq), np.nan)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    ii, jj = np.arange(Nq)[:, None], np.arange(Nk)[None, :]
+    for b, h in pairs:
+        visible = M[h][ii // BLOCK, jj // BLOCK]
+        if causal:
+            visible = visible & (jj <= ii + (Nk - Nq))
+        Q, K, V = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
+        S = np.where(visible, f32_scale(scale) * (Q @ K.T), NEG_INF)
+        m = S.max(axis=1) if Nk > 0 else np.full(Nq, NEG_INF)
+        empty = m == NEG_INF
+        m_shift = np.where(empty, 0.0, m)
+        E = np.exp(S - m_shift[:, None])
+        l = E.sum(axis=1)
+        P = E / np.where(empty, 1.0, l)[:, None]
+        Ob = P @ V
+        Ob[empty] = 0.0
+        O[b, h] = Ob
+        with np.errstate(divide="ignore"):
+            L[b, h] = np.where(empty, NEG_INF, m_shift + np.log(np.where(empty, 1.0, l)))
+    return O, L
+

@@ -482,3 +482,53 @@ def test_grad_planted_mistakes_are_caught():
     }
     for name, (g, which) in slips.items():
         assert not np.allclose(g, want[which], atol=1e-6), name
+
+
+# ---------------------------------------------------------- block sparsity
+
+def _bs_inputs(B, H, Nq, Nk, d, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, H, Nq, d)), rng.standard_normal((B, H, Nk, d)),
+            rng.standard_normal((B, H, Nk, d)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_all_ones_is_dense(causal):
+    q, k, v = _bs_inputs(1, 2, 130, 200, 8, 1)
+    M = np.ones((2, 3, 4), dtype=np.uint8)
+    O1, L1 = oracle.attention_block_sparse(q, k, v, M, 0.3, causal)
+    O2, L2 = oracle.attention(q, k, v, 0.3, causal)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_block_sparse_lower_blocks_plus_diagonal_mask_is_causal():
+    """Admitting exactly the blocks on and below the diagonal and masking
+    inside them is causal attention (Nq = Nk)."""
+    q, k, v = _bs_inputs(1, 1, 192, 192, 8, 2)
+    M = np.tril(np.ones((3, 3), dtype=np.uint8))[None]
+    O1, L1 = oracle.attention_block_sparse(q, k, v, M, 0.3, causal=True)
+    O2, L2 = oracle.attention(q, k, v, 0.3, causal=True)
+    close(O1, O2, 1e-14)
+    close(L1, L2, 1e-14)
+
+
+def test_block_sparse_against_brute_force():
+    """A random block pattern (with an all-masked query block) against the
+    pure-Python definition run on the visible keys of each row."""
+    rng = np.random.default_rng(9)
+    q, k, v = _bs_inputs(1, 2, 70, 150, 3, 3)
+    M = (rng.random((2, 2, 3)) < 0.5).astype(np.uint8)
+    M[1, 1, :] = 0  # a query block that sees nothing
+    M[0, 0, 1] = 1
+    for causal in (False, True):
+        O, L = oracle.attention_block_sparse(q, k, v, M, 0.3, causal)
+        for h in range(2):
+            for i in range(70):
+                keys = [j for j in range(150) if M[h, i // 64, j // 64] and (not causal or j <= i + 80)]
+                if not keys:
+                    assert np.all(O[0, h, i] == 0) and L[0, h, i] == -np.inf
+                    continue
+                Ob, Lb = brute.attention([[[q[0, h, i].tolist()]]], [[[k[0, h, j].tolist() for j in keys]]],
+                                         [[[v[0, h, j].tolist() for j in keys]]], 0.3)
+                close(O[0, h, i], np.array(Ob[0][0][0]), 1e-13)
+                close(L[0, h, i], Lb[0][0][0], 1e-13)
