@@ -13,6 +13,8 @@ One step is one pass of the whole hot path over resident synthetic inputs:
                  H=32, d=128 (token-major [T, H, d], cu_seqlens)
   6. fa_bwd            backward of call 1 (its O and LSE, a seeded dO), fp32
                  gradients, by recomputation
+  7. fa_fwd_block_sparse  call 1's inputs under a 64x64 block mask: a window of
+                 two blocks either side of the diagonal plus the first key block
 The batched decode streams ~8.7 GB, far more than the 256 MB last-level
 cache, so the single-request decode that follows reads its 128 MiB of K/V
 from HBM.  Every call is bracketed by HIP events on the stream it runs on.
@@ -187,6 +189,14 @@ def main():
     bw_ws = torch.empty(fa.fa_bwd_workspace_bytes(P.B, P.H, P.Nq), dtype=torch.uint8, device=dev)
     bw_flops = 2.5 * P.flops()
 
+    # Block-sparse forward of the long prefill's inputs (local window + global block).
+    bs_mask_h = W.block_mask("local_global", P.H, P.Nq, P.Nk)
+    bs_mask = bs_mask_h.to(dev)
+    bs_out = torch.empty_like(q)
+    bs_lse = torch.empty_like(lse)
+    bs_pairs = W.block_mask_pairs(bs_mask_h[:1], P.Nq, P.Nk, True) * P.H * P.B  # same pattern per head
+    bs_flops = 4.0 * P.d * bs_pairs
+
     # A plain copy of known size, untimed: its HBM counters calibrate the
     # prefill kernel's FETCH_SIZE / WRITE_SIZE when this script runs under
     # rocprofv3 --pmc.
@@ -200,7 +210,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(rec):
-        e0, e1, e2, e3, e4, e5, e6 = ev(), ev(), ev(), ev(), ev(), ev(), ev()
+        e0, e1, e2, e3, e4, e5, e6, e7 = ev(), ev(), ev(), ev(), ev(), ev(), ev(), ev()
         e0.record(stream)
         fa.fa_fwd(q, k, v, P.scale, True, out=o, lse=lse)
         e1.record(stream)
@@ -219,8 +229,10 @@ def main():
         fa.fa_bwd(q, k, v, o, bw_do, lse, P.scale, True, dq=bw_dq, dk=bw_dk, dv=bw_dv,
                   workspace=bw_ws)
         e6.record(stream)
+        fa.fa_fwd_block_sparse(q, k, v, bs_mask, P.scale, True, out=bs_out, lse=bs_lse)
+        e7.record(stream)
         if rec is not None:
-            rec.append((e0, e1, e2, e3, e4, e5, e6))
+            rec.append((e0, e1, e2, e3, e4, e5, e6, e7))
 
     for _ in range(args.warmup):
         step(None)
@@ -240,6 +252,7 @@ def main():
     t_pg = [r[3].elapsed_time(r[4]) for r in recs]
     t_vl = [r[4].elapsed_time(r[5]) for r in recs]
     t_bw = [r[5].elapsed_time(r[6]) for r in recs]
+    t_bs = [r[6].elapsed_time(r[7]) for r in recs]
     ms_step = wall * 1e3 / args.steps
 
     flops = P.flops()
@@ -252,6 +265,7 @@ def main():
     pg_gbps = db_bytes / (statistics.mean(t_pg) * 1e-3) / 1e9
     vl_tflops = vl_flops / (statistics.mean(t_vl) * 1e-3) / 1e12
     bw_tflops = bw_flops / (statistics.mean(t_bw) * 1e-3) / 1e12
+    bs_tflops = bs_flops / (statistics.mean(t_bs) * 1e-3) / 1e12
 
     ceil_small, ceil_big = read_ceiling(torch, fa, dev, stream, ds_bytes)
 
@@ -275,7 +289,8 @@ def main():
                         "64 seqs x 32 heads d=128 len U[128,16384] + single decode H=32 N=8192 d=128 "
                         "+ the batched decode over a paged cache (16-token pages) "
                         "+ packed causal prefill 8 seqs x 32 heads d=128 len U[512,8192] "
-                        "+ backward of the causal prefill",
+                        "+ backward of the causal prefill + block-sparse causal prefill "
+                        "(local window of 2 blocks + first block, 64x64 blocks)",
             "prefill": {"B": P.B, "H": P.H, "Nq": P.Nq, "Nk": P.Nk, "d": P.d, "causal": True,
                         "seed": P.seed, "flops": flops, "ms_mean": round(pre_ms, 4),
                         "ms_median": round(statistics.median(t_pre), 4),
@@ -288,6 +303,11 @@ def main():
                               "ms_mean": round(statistics.mean(t_ds), 4)},
             "decode_paged": {"page_size": PAGE, "pages": pg_pages, "split_keys": pg_sk,
                              "kv_bytes": db_bytes, "ms_mean": round(statistics.mean(t_pg), 4)},
+            "block_sparse": {"B": P.B, "H": P.H, "N": P.Nq, "d": P.d, "causal": True,
+                             "mask": "local_global window 2", "block": 64,
+                             "admitted_blocks": int(bs_mask_h.sum()),
+                             "visible_pairs": bs_pairs, "flops": bs_flops,
+                             "ms_mean": round(statistics.mean(t_bs), 4)},
             "backward": {"B": P.B, "H": P.H, "N": P.Nq, "d": P.d, "causal": True,
                          "flops": bw_flops, "ms_mean": round(statistics.mean(t_bw), 4)},
             "prefill_varlen": {"B": VL.B, "H": VL.H, "d": VL.d, "causal": VL.causal,
@@ -317,6 +337,8 @@ def main():
         },
         "varlen": {"unit": "TFLOP/s", "prefill_varlen": round(vl_tflops, 2),
                    "frac_of_bf16_peak": round(vl_tflops / PEAK_BF16_TFLOPS, 4)},
+        "block_sparse": {"unit": "TFLOP/s", "value": round(bs_tflops, 2),
+                         "flops_convention": "4 * d * visible (query, key) pairs"},
         "backward": {"unit": "TFLOP/s", "value": round(bw_tflops, 2),
                      "frac_of_bf16_peak": round(bw_tflops / PEAK_BF16_TFLOPS, 4),
                      "flops_convention": "2.5 x forward (five products of 2*N*N*d, halved causal)"},

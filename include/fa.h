@@ -92,6 +92,25 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                hipStream_t stream);
 
 /*
+ * Block-sparse forward (review §05: long sequences by skipping whole tiles
+ * through a sparsity pattern; the pages give no pattern, so it is an input).
+ * Key j is visible to query i only if block_mask admits the pair of 64-row /
+ * 64-key blocks, and with causal != 0 also j <= i + Nk - Nq.  Tiles the mask
+ * excludes for a whole workgroup of 256 queries are neither loaded nor
+ * computed.
+ *
+ *   block_mask  uint8 [H, ceil(Nq / 64), ceil(Nk / 64)] (device), nonzero =
+ *               admitted; shared by the batch
+ *   the rest    as for fa_fwd; d must be 128 (else FA_ERR_UNSUPPORTED) and
+ *               ceil(Nk / 64) <= 1024
+ *
+ * A row with no visible key gets O = 0 and LSE = -inf.
+ */
+int fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const uint8_t* block_mask, int B, int H, int Nq, int Nk, int d,
+                        float scale, int causal, hipStream_t stream);
+
+/*
  * Backward pass by recomputation (review §03: the forward keeps only O and the
  * row statistics; the backward rebuilds the score and probability blocks on
  * chip).  Gradients of L with respect to q, k, v for a given dL/dO, for the

@@ -10,6 +10,7 @@ exception is raised.
     o, lse = fa_fwd_f32(q, k, v, scale, causal)        # fp32 [B,H,N,d]
     o, lse = fa_fwd_varlen(q, k, v, cu_q, cu_k, max_q, scale, causal)  # packed [T,H,d]
     dq, dk, dv = fa_bwd(q, k, v, o, dout, lse, scale, causal)          # fp32 gradients
+    o, lse = fa_fwd_block_sparse(q, k, v, block_mask, scale, causal)   # 64x64 block mask
     o, lse = fa_decode_varlen(q, kcache, vcache, seqlens, offsets, max_seqlen, scale)
     o, lse = fa_decode_paged(q, kpages, vpages, block_table, seqlens, max_seqlen, scale)
 """
@@ -35,6 +36,7 @@ _Z = ctypes.c_size_t
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -149,6 +151,38 @@ def fa_fwd_f32(q, k, v, scale=None, causal=False, out=None, lse=None, stream=Non
 
 def fa_decode_split_keys(B, H, d, max_seqlen) -> int:
     return int(load().fa_decode_split_keys(B, H, d, max_seqlen))
+
+
+def fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False, out=None, lse=None,
+                        stream=None):
+    """Block-sparse forward: q [B,H,Nq,128], k/v [B,H,Nk,128] bf16; block_mask
+    uint8 [H, ceil(Nq/64), ceil(Nk/64)] on the device (nonzero = admitted).
+    Returns (O bf16 [B,H,Nq,128], LSE fp32 [B,H,Nq])."""
+    import torch
+
+    lib = load()
+    pq = _dev(q, "q", torch.bfloat16, 4)
+    pk = _dev(k, "k", torch.bfloat16, 4)
+    pv = _dev(v, "v", torch.bfloat16, 4)
+    pm = _dev(block_mask, "block_mask", torch.uint8, 3)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError("q, k, v shapes disagree")
+    if tuple(block_mask.shape) != (H, -(-Nq // 64), -(-Nk // 64)):
+        raise ValueError("block_mask must be [H, ceil(Nq/64), ceil(Nk/64)]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    po = _dev(out, "out", torch.bfloat16, 4)
+    pl = _dev(lse, "lse", torch.float32, 3)
+    st = lib.fa_fwd_block_sparse(pq, pk, pv, po, pl, pm, B, H, Nq, Nk, d, float(scale),
+                                 1 if causal else 0, _stream(q, stream))
+    _check(st, "fa_fwd_block_sparse")
+    return out, lse
 
 
 def fa_bwd_workspace_bytes(B, H, Nq) -> int:

@@ -14,6 +14,8 @@ constexpr long long kMaxGridX = 0x7fffffffLL;  // HIP grid.x limit
 constexpr long long kMaxGridYZ = 65535;
 constexpr long long kMaxChunks = 256;  // chunks per sequence the merge kernel combines
 constexpr long long kMaxPageSize = 1 << 16;   // tokens per page of a paged cache
+constexpr int kSparseBlock = 64;              // rows and keys per block-sparse mask block
+constexpr int kMaxSparseKeyBlocks = 1024;     // key blocks a block-sparse walk may list
 constexpr long long kMaxChunkPages = 1024;    // pages one chunk may span (staged in LDS)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -103,6 +105,25 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
   a.total_q = total_q;
+  return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const uint8_t* block_mask, int B, int H, int Nq, int Nk, int d,
+                        float scale, int causal, hipStream_t stream) {
+  if (!block_mask) return FA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (!dims_ok(B, H, Nq, Nk)) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if ((Nk + kSparseBlock - 1) / kSparseBlock > kMaxSparseKeyBlocks) return FA_ERR_INVALID_ARG;
+  if (fa::fwd_bf16_grid(B, H, Nq) > kMaxGridX) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal ? 1 : 0, stream};
+  a.bmask = block_mask;
+  a.nqb = (Nq + kSparseBlock - 1) / kSparseBlock;
+  a.nkb = (Nk + kSparseBlock - 1) / kSparseBlock;
   return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

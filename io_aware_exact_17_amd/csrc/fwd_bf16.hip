@@ -74,6 +74,7 @@ constexpr int kBR = 256;             // query rows per workgroup (4 waves x 64)
 constexpr int kBC = 64;              // keys per staged tile (two 32-key blocks)
 constexpr int kNBuf = 4;             // LDS buffers per operand
 constexpr float kSumBound = 256.f;   // a block's P sum per lane stays <= 2^8
+constexpr int kMaxSparseTiles = 1024;  // key tiles a block-sparse walk may list (Nk <= 65536)
 
 template <int D>
 struct FwdCfg {
@@ -193,12 +194,18 @@ struct QuarterOps {
 // rows cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1, LSE
 // [H, total_q]; grid (the longest sequence's query tiles x H, B).
 // Otherwise [B, H, N, d] with contiguous rows per head.
-template <int D, bool CAUSAL, bool VARLEN>
+//
+// SPARSE (dense layout only): key j is visible to query i only where the
+// block mask [H, nqb, nkb] (64 x 64 blocks) admits the pair.  A wave's 64
+// rows are one mask row; the workgroup walks the compacted list of key tiles
+// any of its four mask rows admits, and a wave whose own row does not admit
+// a listed tile masks all of it.
+template <int D, bool CAUSAL, bool VARLEN, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int Nq_dense, int Nk_dense,
     float c, int n_qtiles, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
-    int H, int total_q) {
+    int H, int total_q, const uint8_t* __restrict__ bmask, int nqb, int nkb) {
   using C = FwdCfg<D>;
   using Ops = QuarterOps<D>;
   constexpr int TB = C::TILE * 2;        // bytes per K or V tile
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group this lane holds
 
   // Heaviest query tile first; heads vary fastest.
-  int qt, Nq, Nk;
+  int qt, Nq, Nk, head;
   size_t qbase, kbase, lse_base;  // elements
   if constexpr (VARLEN) {
     // One sequence after another (grid.y), so the workgroups running
@@ -229,12 +236,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     Nq = cu_q[b + 1] - qs;
     Nk = cu_k[b + 1] - ks;
     if (qt * kBR >= Nq) return;  // past this sequence's last query tile
+    head = h;
     qbase = ((size_t)qs * H + h) * D;
     kbase = ((size_t)ks * H + h) * D;
     lse_base = (size_t)h * total_q + qs;
   } else {
     qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
     const int bh = (int)(blockIdx.x % BH);
+    head = bh % max(H, 1);
     Nq = Nq_dense;
     Nk = Nk_dense;
     qbase = (size_t)bh * Nq * D;
@@ -248,13 +257,79 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int off = Nk - Nq;  // bottom-right causal alignment
 
   const int kv_end = CAUSAL ? min(Nk, q0 + kBR + off) : Nk;
-  const int n_tiles = kv_end > 0 ? (kv_end + kBC - 1) / kBC : 0;
+  const int n_cand = kv_end > 0 ? (kv_end + kBC - 1) / kBC : 0;  // key tiles in causal reach
 
   const int wq0 = q0 + wave * 64;  // first query row of this wave
   const int qi0 = wq0 + col;       // this lane's row in row block 0 (+32 in block 1)
   const int kv_end_w = CAUSAL ? min(Nk, wq0 + 64 + off) : Nk;
-  const int nbw = kv_end_w > 0 ? (kv_end_w + 31) / 32 : 0;  // 32-key blocks this wave needs
-  const int njw = (nbw + 1) / 2;                             // tiles this wave needs
+
+  // Block-sparse: the list of key tiles (s_tile) that any of the four mask
+  // rows of the workgroup admits, in order, with the admitting waves as bits
+  // (s_vis); compacted with one ballot per wave and 256 candidates per pass.
+  __shared__ uint16_t s_tile[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ uint8_t s_vis[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ int s_cnt[SPARSE ? kWaves : 1];
+  int n_list = n_cand, nbw, njw;
+  if constexpr (SPARSE) {
+    const uint8_t* mrow = bmask + ((size_t)head * nqb + 4 * qt) * nkb;
+    n_list = 0;
+    for (int base = 0; base < n_cand; base += kThreads) {
+      const int t = base + tid;
+      unsigned vis = 0;
+      if (t < n_cand) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          if (4 * qt + w < nqb && mrow[(size_t)w * nkb + t]) vis |= 1u << w;
+      }
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(vis != 0);
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (lane == 0) s_cnt[wave] = __builtin_popcountll(bal);
+      __syncthreads();
+      int at = n_list;
+      for (int w = 0; w < wave; ++w) at += s_cnt[w];
+      if (vis) {
+        s_tile[at + below] = (uint16_t)t;
+        s_vis[at + below] = (uint8_t)vis;
+      }
+      n_list += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+      __syncthreads();
+    }
+    // Listed tiles this wave's rows can reach causally (the list is sorted).
+    const int lim_tile = kv_end_w > 0 ? (kv_end_w + kBC - 1) / kBC : 0;
+    int cnt = 0;
+    for (int i0 = 0; i0 < n_list; i0 += 64) {
+      const int i = i0 + lane;
+      const int ti = s_tile[min(i, kMaxSparseTiles - 1)];
+      cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n_list && ti < lim_tile));
+    }
+    njw = cnt;
+    nbw = 2 * njw;
+  } else {
+    nbw = kv_end_w > 0 ? (kv_end_w + 31) / 32 : 0;  // 32-key blocks this wave needs
+    njw = (nbw + 1) / 2;                             // tiles this wave needs
+  }
+  const int n_tiles = n_list;
+  // Key tile of list entry j (the identity when dense).  The walk also
+  // forms the scores of the block after the last one; past the list that is
+  // a tile beyond Nk, masked whole as in the dense walk.
+  auto tile_of = [&](int j) -> int {
+    if constexpr (SPARSE)
+      return j < n_tiles ? __builtin_amdgcn_readfirstlane((int)s_tile[j]) : (Nk + kBC - 1) / kBC;
+    else
+      return j;
+  };
+  // First key of 32-key block b of the walk.
+  auto key_pos = [&](int b) -> int {
+    if constexpr (SPARSE) return tile_of(b >> 1) * kBC + 32 * (b & 1);
+    else return 32 * b;
+  };
+  auto admitted = [&](int b) -> bool {
+    if constexpr (SPARSE)
+      return (b >> 1) < n_tiles && ((__builtin_amdgcn_readfirstlane((int)s_vis[b >> 1]) >> wave) & 1);
+    else
+      return true;
+  };
 
   // Q^T operands: lane holds Q[row][16s + 8*half + 0..7] of both row blocks.
   // Rows past Nq read row Nq-1 (their results are never stored).
@@ -288,15 +363,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const char* const vg = reinterpret_cast<const char*>(V + kbase);
   const uint32_t lds_wave = (uint32_t)(size_t)lds + wave * C::IPW * 1024;
   auto issue = [&](const char* base, int region, int j) {
-    const char* t = base + (size_t)j * kBC * kv_rsb;
+    const int tj = tile_of(j);
+    const char* t = base + (size_t)tj * kBC * kv_rsb;
     uint32_t dst = lds_wave;
     asm volatile("" : "+s"(dst));
     dst += region;
-    if ((j + 1) * kBC <= Nk) {
+    if ((tj + 1) * kBC <= Nk) {
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i) copy_to_lds(t, g_off[i], dst + i * 1024);
     } else {
-      const int last = Nk - 1 - j * kBC;
+      const int last = Nk - 1 - tj * kBC;
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i) {
         const int r = (wave * C::IPW + i) * C::RPI + ld_row;
@@ -374,11 +450,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // 32b + 4h + 8(r/4) + r%4; it is visible to row block rb iff that key is
   // <= lim(rb), i.e. iff 8(r/4) + r%4 <= lim(rb) - 32b - 4h.
   auto needs_mask = [&](int b) {
-    return (32 * b + 32 > Nk) || (CAUSAL && 32 * b + 31 > wq0 + off);
+    const int kp = key_pos(b);
+    return (kp + 32 > Nk) || (CAUSAL && kp + 31 > wq0 + off) || !admitted(b);
   };
   auto mask_room = [&](int b, int rb) {
     const int lim = CAUSAL ? min(Nk - 1, qi0 + 32 * rb + off) : Nk - 1;
-    return lim - 32 * b - 4 * half;
+    return admitted(b) ? lim - key_pos(b) - 4 * half : -(1 << 20);
   };
 
   // P = 2^(s*c - m) against the current reference (0 where masked) for
@@ -765,7 +842,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool SPARSE>
 hipError_t launch(const FwdArgs& a) {
   const int n_qtiles = (a.Nq + kBR - 1) / kBR;
   const int BH = a.B * a.H;
@@ -775,19 +852,21 @@ hipError_t launch(const FwdArgs& a) {
   const dim3 grid = VARLEN ? dim3((unsigned)(n_qtiles * a.H), (unsigned)a.B)
                            : dim3((unsigned)(n_qtiles * BH));
   const dim3 block(kThreads);
-  void* args[] = {(void*)&a.q,    (void*)&a.k,    (void*)&a.v,  (void*)&a.o,       (void*)&a.lse,
-                  (void*)&BH,     (void*)&a.Nq,   (void*)&a.Nk, (void*)&c,         (void*)&n_qtiles,
-                  (void*)&a.cu_q, (void*)&a.cu_k, (void*)&a.H,  (void*)&a.total_q};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL, VARLEN>), grid,
-                         block, args, 0, a.stream);
+  void* args[] = {(void*)&a.q,     (void*)&a.k,    (void*)&a.v,  (void*)&a.o,       (void*)&a.lse,
+                  (void*)&BH,      (void*)&a.Nq,   (void*)&a.Nk, (void*)&c,         (void*)&n_qtiles,
+                  (void*)&a.cu_q,  (void*)&a.cu_k, (void*)&a.H,  (void*)&a.total_q, (void*)&a.bmask,
+                  (void*)&a.nqb,   (void*)&a.nkb};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL, VARLEN, SPARSE>),
+                         grid, block, args, 0, a.stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
   if (a.d != 128) return launch_fwd_bf16_d64(a);
-  if (a.cu_q) return a.causal ? launch<128, true, true>(a) : launch<128, false, true>(a);
-  return a.causal ? launch<128, true, false>(a) : launch<128, false, false>(a);
+  if (a.cu_q) return a.causal ? launch<128, true, true, false>(a) : launch<128, false, true, false>(a);
+  if (a.bmask) return a.causal ? launch<128, true, false, true>(a) : launch<128, false, false, true>(a);
+  return a.causal ? launch<128, true, false, false>(a) : launch<128, false, false, false>(a);
 }
 
 long long fwd_bf16_grid(int B, int H, int Nq) {

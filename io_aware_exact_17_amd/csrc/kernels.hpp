@@ -25,6 +25,10 @@ struct FwdArgs {
   const int32_t* cu_q = nullptr;
   const int32_t* cu_k = nullptr;
   int total_q = 0;
+  // Block-sparse mask (d = 128, dense layout): uint8 [H, nqb, nkb] over
+  // 64 x 64 blocks, null when every block is admitted.
+  const uint8_t* bmask = nullptr;
+  int nqb = 0, nkb = 0;
 };
 
 struct DecodeArgs {

@@ -177,3 +177,14 @@ def test_decode_paged_split_plan():
     assert sk % 64 == 0 and sk + 1 <= 1024
     assert fa.fa_decode_paged_split_keys(1, 1, 128, 100, 3) == 0
 
+
+
+def test_block_sparse_rejects_invalid_arguments():
+    lib = fa.load()
+    call = lambda **kw: lib.fa_fwd_block_sparse(  # noqa: E731
+        kw.get("q", A), A, A, A2, A2, kw.get("m", A2), 1, 2, kw.get("Nq", 64), kw.get("Nk", 64),
+        kw.get("d", 128), 0.1, 0, None)
+    assert call(m=None) == INVALID
+    assert call(q=A + 8) == INVALID
+    assert call(d=64) == UNSUPPORTED
+    assert call(Nk=64 * 1024 + 1) == INVALID  # more than 1024 key blocks

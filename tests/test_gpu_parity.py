@@ -351,6 +351,57 @@ def test_bwd_full_size_one_head(fa):
     check_grads((dq[0, h], dk[0, h], dv[0, h]), want, f"head {h}")
 
 
+SPARSE_CASES = [
+    # (kind, causal, Nq, Nk)
+    ("random", False, 300, 300),
+    ("random", True, 300, 300),
+    ("random", True, 200, 700),
+    ("random", False, 700, 130),
+    ("local_global", True, 1024, 1024),
+    ("local_global", False, 520, 900),
+    ("zeros", False, 256, 256),
+]
+
+
+@pytest.mark.parametrize("kind,causal,Nq,Nk", SPARSE_CASES)
+def test_fwd_block_sparse(fa, kind, causal, Nq, Nk):
+    log(f"case block sparse {kind} causal={causal} Nq={Nq} Nk={Nk}")
+    B, H, d = 2, 3, 128
+    q, k, v = W.prefill_inputs(B, H, Nq, Nk, d, "bf16", seed=Nq + 3 * Nk, device="cuda")
+    m = W.block_mask(kind, H, Nq, Nk, seed=Nq)
+    o, lse = fa.fa_fwd_block_sparse(q, k, v, m.to("cuda"), 0.088, causal)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_block_sparse(q, k, v, m, 0.088, causal)
+    check(o, lse, O, L, TOL_BF16, f"block sparse {kind}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_block_sparse_all_ones_equals_dense(fa, causal):
+    """Every block admitted: the same tiles in the same order as the dense
+    kernel, so the results are identical."""
+    B, H, N, d = 1, 4, 777, 128
+    q, k, v = W.prefill_inputs(B, H, N, N, d, "bf16", seed=31, device="cuda")
+    o, lse = fa.fa_fwd(q, k, v, 0.088, causal)
+    o2, lse2 = fa.fa_fwd_block_sparse(q, k, v, W.block_mask("ones", H, N, N).to("cuda"), 0.088,
+                                      causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_fwd_block_sparse_full_size_one_head(fa):
+    """N=8192, H=32, causal, local window of 2 blocks each side plus the first
+    key block: one head against the oracle."""
+    s = W.LONG_PREFILL
+    log(f"case block sparse {s.name} local_global")
+    q, k, v = W.prefill_spec_inputs(s, "cuda")
+    m = W.block_mask("local_global", s.H, s.Nq, s.Nk)
+    o, lse = fa.fa_fwd_block_sparse(q, k, v, m.to("cuda"), s.scale, s.causal)
+    torch.cuda.synchronize()
+    h = 5
+    O, L = oracle.attention_block_sparse(q, k, v, m, s.scale, s.causal, heads=[(0, h)])
+    check(o[0, h], lse[0, h], O[0, h], L[0, h], TOL_BF16, f"head {h}")
+
+
 def paged_copy(kc, vc, sl, off, page_size, seed, spare=3, max_len=None):
     bt, npg = W.paged_layout(sl, page_size, seed=seed, spare_pages=spare, max_len=max_len)
     kp = W.to_pages(kc, sl, off, bt, page_size, npg)

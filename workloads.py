@@ -233,6 +233,43 @@ def varlen_spec_inputs(spec: VarlenSpec, device="cpu"):
     return (lens,) + varlen_inputs(lens, lens, spec.H, spec.d, spec.seed, device)
 
 
+def block_mask(kind, H, Nq, Nk, seed=0, window=2, density=0.5):
+    """A uint8 block mask [H, ceil(Nq/64), ceil(Nk/64)] over 64 x 64 blocks:
+    "ones", "zeros", "random" (each block admitted with `density`), or
+    "local_global" (query block i admits key blocks i-window .. i+window
+    after aligning the ends, plus key block 0 for every query block)."""
+    nqb, nkb = -(-Nq // 64), -(-Nk // 64)
+    if kind == "ones":
+        return torch.ones((H, nqb, nkb), dtype=torch.uint8)
+    if kind == "zeros":
+        return torch.zeros((H, nqb, nkb), dtype=torch.uint8)
+    if kind == "random":
+        g = _gen("cpu", seed)
+        return (torch.rand((H, nqb, nkb), generator=g) < density).to(torch.uint8)
+    if kind == "local_global":
+        i = torch.arange(nqb)[:, None] + (nkb - nqb)
+        j = torch.arange(nkb)[None, :]
+        m = ((j - i).abs() <= window) | (j == 0)
+        return m.to(torch.uint8)[None].expand(H, nqb, nkb).contiguous()
+    raise ValueError(kind)
+
+
+def block_mask_pairs(mask, Nq, Nk, causal):
+    """Visible (query, key) pairs of a block mask (summed over heads): the
+    algorithmic work of a block-sparse pass is 4 * d * pairs FLOPs per batch."""
+    M = torch.as_tensor(mask).to(torch.bool)
+    H, nqb, nkb = M.shape
+    rows = torch.arange(Nq)
+    cols = torch.arange(Nk)
+    total = 0
+    for h in range(H):
+        vis = M[h][rows[:, None] // 64, cols[None, :] // 64]
+        if causal:
+            vis = vis & (cols[None, :] <= rows[:, None] + (Nk - Nq))
+        total += int(vis.sum())
+    return total
+
+
 def decode_kv_bytes(seqlens, H, d, elem_bytes=2) -> int:
     """Bytes of K plus V history the decode step must read."""
     T = int(torch.as_tensor(seqlens).to(torch.int64).sum())
