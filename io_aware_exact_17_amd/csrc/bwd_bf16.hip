@@ -87,6 +87,66 @@ __device__ __forceinline__ bf16x8 tr_op(const lds_char* tile, int lane, int db, 
   return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
 }
 
+// Matrix products written as single instructions so that the score products
+// land in vector registers (the row work reads them) and the gradient
+// accumulators stay in accumulation registers for the whole pass (as a
+// compiled product the compiler moves them between register files every
+// block).  The compiler does not see these as matrix instructions, so it
+// inserts none of the wait states their results need: each pause below
+// takes the registers it guards as operands, which puts every later reader
+// of them after the pause.
+// The score products take their fixed B operand (the rows a workgroup keeps
+// for the whole pass) from accumulation registers: held there, it is never
+// copied into vector registers by the vector unit just before a product
+// reads it (a hazard the compiler does not guard for these statements).
+__device__ __forceinline__ void mm_first(f32x16& d, bf16x8 a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mm_next(f32x16& d, bf16x8 a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mm_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// Zeroed accumulators, produced in accumulation registers by a product of
+// zero operands: every value the accumulators take is then defined there, and
+// the compiler keeps them there across the loop instead of holding them in
+// vector registers and copying them over around each product.
+template <int N>
+__device__ __forceinline__ void zero_acc(f32x16 (&a)[N]) {
+  bf16x8 z = {};
+  asm volatile("s_nop 4" : "+v"(z));  // the zeros are written by the vector unit
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(a[i]) : "v"(z));
+}
+
+// Before vector instructions read the two score products.
+__device__ __forceinline__ void pause_scores(f32x16& a, f32x16& b) {
+  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(a), "+v"(b));
+}
+// Before the accumulators are read out, after the last product into them.
+template <int N>
+__device__ __forceinline__ void pause_acc(f32x16 (&a)[N]) {
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(a[i]));
+}
+// Before a product reads B operands the vector unit has just written.
+__device__ __forceinline__ void pause_operands(bf16x8 (&a)[2]) {
+  asm volatile("s_nop 4" : "+v"(a[0]), "+v"(a[1]));
+}
+__device__ __forceinline__ void pause_operands(bf16x8 (&a)[2], bf16x8 (&b)[2]) {
+  asm volatile("s_nop 4" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]));
+}
+
+// Returns the tile pointers unchanged, but only after every matrix
+// instruction issued above it: loads addressed through the results are not
+// moved ahead of those products (which would hold their registers longer).
+__device__ __forceinline__ void after_products(const lds_char*& a, const lds_char*& b) {
+  asm volatile("" : "+s"(a), "+s"(b));
+}
+
 // Accumulator registers 8t .. 8t+7 packed to bf16 as a B operand.
 __device__ __forceinline__ bf16x8 pack_b(const float (&x)[16], int t) {
   return __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(x[8 * t], x[8 * t + 1]),
@@ -180,10 +240,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const float* l2h = lse2 + (size_t)bh * Nq;
   const float* Dh = Dv + (size_t)bh * Nq;
 
-  // Query blocks that see any key of the workgroup / of this wave.
+  // Query blocks that see any key of the workgroup.  Every wave takes every
+  // one of them: a block that sees none of the wave's keys lies above the
+  // diagonal for all of them, so the causal mask zeroes its P and dS (the
+  // few blocks this costs are cheaper than a branch around the body, across
+  // which the compiler moves the accumulators).
   const int n_qb = (Nq + kRows - 1) / kRows;
   const int qb_first = CAUSAL ? max(0, kt * kFixed - off) / kRows : 0;
-  const int qb_wave = CAUSAL ? max(0, k0w - off) / kRows : 0;
 
   // Fixed operands: K and V rows of this wave's keys as B operands.
   bf16x8 kf[T::KS], vf[T::KS];
@@ -193,8 +256,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     vf[s] = load_row_op<D>(V + (size_t)bh * Nk * D, k0w + col, Nk, lane, s);
   }
   f32x16 dk[T::NDB], dv[T::NDB];
-#pragma unroll
-  for (int i = 0; i < T::NDB; ++i) dk[i] = dv[i] = f32x16{};
+  zero_acc(dk);
+  zero_acc(dv);
 
   Stager<D> sq, sd;
   float st = 0.f;  // this thread's lse2 or D value of the next block (threads 0..63)
@@ -220,43 +283,90 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   for (int qb = qb_first; qb < n_qb; ++qb) {
     const int buf = (qb - qb_first) & 1;
     if (qb + 1 < n_qb) fetch(qb + 1);
-    if (qb >= qb_wave) {
+    {
       const lds_char* qt = q_tile(buf);
       const lds_char* dt = do_tile(buf);
       // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys:
       // lane = key (column), register r = query 8(r/4) + 4 half + r%4.
-      f32x16 S = {}, dP = {};
+      // All operands first (the block's lse2 and D values with them), then
+      // the products.
+      const auto* stp = reinterpret_cast<const __attribute__((address_space(3))) float*>(st_tile(buf));
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l4[g] = *reinterpret_cast<const lds_f32x4*>(stp + 8 * g + 4 * half);
+        d4[g] = *reinterpret_cast<const lds_f32x4*>(stp + kRows + 8 * g + 4 * half);
+      }
+      bf16x8 qa[T::KS], da[T::KS];
 #pragma unroll
       for (int s = 0; s < T::KS; ++s) {
-        S = mfma_32x32x16(row_op<D>(qt, lane, s), kf[s], S);
-        dP = mfma_32x32x16(row_op<D>(dt, lane, s), vf[s], dP);
+        qa[s] = row_op<D>(qt, lane, s);
+        da[s] = row_op<D>(dt, lane, s);
       }
-      const auto* stp = reinterpret_cast<const __attribute__((address_space(3))) float*>(st_tile(buf));
+      f32x16 S, dP;
+      mm_first(S, qa[0], kf[0]);
+      mm_first(dP, da[0], vf[0]);
+#pragma unroll
+      for (int s = 1; s < T::KS; ++s) {
+        mm_next(S, qa[s], kf[s]);
+        mm_next(dP, da[s], vf[s]);
+      }
+      // transposed operands of the first 16 queries, read during the wait
+      bf16x8 tdo[T::NDB], tq[T::NDB];
+#pragma unroll
+      for (int db = 0; db < T::NDB; ++db) {
+        tdo[db] = tr_op<D>(dt, lane, db, 0);
+        tq[db] = tr_op<D>(qt, lane, db, 0);
+      }
+      pause_scores(S, dP);
       float P[16], dS[16];
       const int key = k0w + col;
       const bool diag = CAUSAL && k0w + kRows - 1 > qb * kRows + off;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(stp + 8 * g + 4 * half);
-        const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(stp + kRows + 8 * g + 4 * half);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * g + i;
-          float p = exp2_hw(S[r] * c - l4[i]);
+          float p = exp2_hw(S[r] * c - l4[g][i]);
           if (diag && key > qb * kRows + 8 * g + 4 * half + i + off) p = 0.f;
           P[r] = p;
-          dS[r] = p * (dP[r] - d4[i]);
+          dS[r] = p * (dP[r] - d4[g][i]);
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 queries.
+      bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 pb = pack_b(P, t), sb = pack_b(dS, t);
+        pb[t] = pack_b(P, t);
+        sb[t] = pack_b(dS, t);
+      }
+      pause_operands(pb, sb);
+      // The first 16 queries' products; the last 16 queries' operands are
+      // read while the second half of them runs.
+      constexpr int H1 = T::NDB / 2;
 #pragma unroll
-        for (int db = 0; db < T::NDB; ++db) {
-          dv[db] = mfma_32x32x16(tr_op<D>(dt, lane, db, t), pb, dv[db]);
-          dk[db] = mfma_32x32x16(tr_op<D>(qt, lane, db, t), sb, dk[db]);
-        }
+      for (int db = 0; db < H1; ++db) {
+        mm_acc(dv[db], tdo[db], pb[0]);
+        mm_acc(dk[db], tq[db], sb[0]);
+      }
+      const lds_char* qt1 = qt;
+      const lds_char* dt1 = dt;
+      after_products(qt1, dt1);
+      bf16x8 udo[T::NDB], uq[T::NDB];
+#pragma unroll
+      for (int db = 0; db < T::NDB; ++db) {
+        udo[db] = tr_op<D>(dt1, lane, db, 1);
+        uq[db] = tr_op<D>(qt1, lane, db, 1);
+      }
+#pragma unroll
+      for (int db = H1; db < T::NDB; ++db) {
+        mm_acc(dv[db], tdo[db], pb[0]);
+        mm_acc(dk[db], tq[db], sb[0]);
+      }
+#pragma unroll
+      for (int db = 0; db < T::NDB; ++db) {
+        mm_acc(dv[db], udo[db], pb[1]);
+        mm_acc(dk[db], uq[db], sb[1]);
       }
     }
     if (qb + 1 < n_qb) {
@@ -269,6 +379,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   // dK^T / dV^T accumulators: lane = key, register r of dim block db =
   // dim 32 db + 8(r/4) + 4 half + r%4.
+  pause_acc(dk);
+  pause_acc(dv);
   const int key = k0w + col;
   if (key < Nk) {
     float* dKr = dK + ((size_t)bh * Nk + key) * D;
@@ -313,11 +425,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const bf16* Kh = K + (size_t)bh * Nk * D;
   const bf16* Vh = V + (size_t)bh * Nk * D;
 
-  // Key blocks any query of the workgroup / of this wave sees.
+  // Key blocks any query of the workgroup sees (every wave takes all of them).
   const int kv_end = CAUSAL ? min(Nk, min(Nq, (qt + 1) * kFixed) + off) : Nk;
   const int n_kb = kv_end > 0 ? (kv_end + kRows - 1) / kRows : 0;
-  const int kv_end_w = CAUSAL ? min(Nk, min(Nq, q0w + kRows) + off) : Nk;
-  const int n_kb_w = kv_end_w > 0 ? (kv_end_w + kRows - 1) / kRows : 0;
 
   bf16x8 qf[T::KS], df[T::KS];
 #pragma unroll
@@ -328,8 +438,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const float l2 = q < Nq ? lse2[(size_t)bh * Nq + q] : __builtin_huge_valf();
   const float dq_row = q < Nq ? Dv[(size_t)bh * Nq + q] : 0.f;
   f32x16 acc[T::NDB];
-#pragma unroll
-  for (int i = 0; i < T::NDB; ++i) acc[i] = f32x16{};
+  zero_acc(acc);
 
   Stager<D> sk, sv;
   if (n_kb > 0) {
@@ -345,17 +454,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
       sk.fetch(Kh, (kb + 1) * kRows, Nk, tid);
       sv.fetch(Vh, (kb + 1) * kRows, Nk, tid);
     }
-    if (kb < n_kb_w) {
+    {  // blocks past this wave's last visible key are masked whole
       const lds_char* kt_ = k_tile(buf);
       const lds_char* vt = v_tile(buf);
       // S^T = K Q^T and dP^T = V dO^T: lane = query (column), register r =
-      // key 8(r/4) + 4 half + r%4 of the block.
-      f32x16 S = {}, dP = {};
+      // key 8(r/4) + 4 half + r%4 of the block.  All operands first.
+      bf16x8 ka[T::KS], va[T::KS];
 #pragma unroll
       for (int s = 0; s < T::KS; ++s) {
-        S = mfma_32x32x16(row_op<D>(kt_, lane, s), qf[s], S);
-        dP = mfma_32x32x16(row_op<D>(vt, lane, s), df[s], dP);
+        ka[s] = row_op<D>(kt_, lane, s);
+        va[s] = row_op<D>(vt, lane, s);
       }
+      f32x16 S, dP;
+      mm_first(S, ka[0], qf[0]);
+      mm_first(dP, va[0], df[0]);
+#pragma unroll
+      for (int s = 1; s < T::KS; ++s) {
+        mm_next(S, ka[s], qf[s]);
+        mm_next(dP, va[s], df[s]);
+      }
+      bf16x8 tk[2][T::NDB];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) tk[t][db] = tr_op<D>(kt_, lane, db, t);
+      pause_scores(S, dP);
       const int k0 = kb * kRows;
       const bool edge = k0 + kRows > Nk || (CAUSAL && k0 + kRows - 1 > q0w + off);
       float dS[16];
@@ -367,12 +490,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
         dS[r] = p * (dP[r] - dq_row);
       }
       // dQ^T += K^T dS^T over the block's 32 keys.
+      bf16x8 sb[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 sb = pack_b(dS, t);
+      for (int t = 0; t < 2; ++t) sb[t] = pack_b(dS, t);
+      pause_operands(sb);
 #pragma unroll
-        for (int db = 0; db < T::NDB; ++db) acc[db] = mfma_32x32x16(tr_op<D>(kt_, lane, db, t), sb, acc[db]);
-      }
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) mm_acc(acc[db], tk[t][db], sb[t]);
     }
     if (kb + 1 < n_kb) {
       sk.store(k_tile(buf ^ 1), tid);  // last read in the previous iteration
@@ -381,6 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     }
   }
 
+  pause_acc(acc);
   if (q < Nq) {
     float* dQr = dQ + ((size_t)bh * Nq + q) * D;
 #pragma unroll
