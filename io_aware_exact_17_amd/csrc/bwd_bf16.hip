@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 // (late queries, which see the most keys, first).  The key blocks stream
 // through LDS (K, V), double-buffered.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dv,
     float* __restrict__ dQ, int BH, int Nq, int Nk, float c, float scale, int n_qt) {
@@ -440,44 +440,74 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   f32x16 acc[T::NDB];
   zero_acc(acc);
 
-  Stager<D> sk, sv;
+  // K and V blocks go from memory straight into LDS (no staging registers):
+  // copy i of a wave fills tile bytes 1024 (wave IPW + i) .. +1023, lane l
+  // the 16 bytes of row p / CPR, slot p % CPR (p = 64 (wave IPW + i) + l),
+  // so the lane fetches the chunk that slot holds.  Rows past Nk fetch row
+  // Nk-1 (finite values whose P is masked to 0).
+  constexpr int IPW = T::BYTES / 1024 / kWaves;
+  const char* const kg = reinterpret_cast<const char*>(Kh);
+  const char* const vg = reinterpret_cast<const char*>(Vh);
+  const uint32_t lds_wave = (uint32_t)(size_t)lds + wave * IPW * 1024;
+  auto stage = [&](int kb, int buf) {
+    uint32_t dst = lds_wave;
+    asm volatile("" : "+s"(dst));
+    dst += buf * 2 * T::BYTES;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int p = (wave * IPW + i) * 64 + lane;
+      const int r = p / T::CPR, slot = p % T::CPR;
+      const uint32_t off = (uint32_t)(min(kb * kRows + r, Nk - 1) * T::ROWB + swz<D>(r, slot) * 16);
+      copy_to_lds(kg, off, dst + i * 1024);
+      copy_to_lds(vg, off, dst + T::BYTES + i * 1024);
+    }
+  };
   if (n_kb > 0) {
-    sk.fetch(Kh, 0, Nk, tid);
-    sv.fetch(Vh, 0, Nk, tid);
-    sk.store(k_tile(0), tid);
-    sv.store(v_tile(0), tid);
+    stage(0, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
   }
   for (int kb = 0; kb < n_kb; ++kb) {
     const int buf = kb & 1;
-    if (kb + 1 < n_kb) {
-      sk.fetch(Kh, (kb + 1) * kRows, Nk, tid);
-      sv.fetch(Vh, (kb + 1) * kRows, Nk, tid);
-    }
+    // buffer buf ^ 1 was last read in the previous iteration, which every
+    // wave finished before that iteration's barrier
+    if (kb + 1 < n_kb) stage(kb + 1, buf ^ 1);
     {  // blocks past this wave's last visible key are masked whole
       const lds_char* kt_ = k_tile(buf);
       const lds_char* vt = v_tile(buf);
       // S^T = K Q^T and dP^T = V dO^T: lane = query (column), register r =
-      // key 8(r/4) + 4 half + r%4 of the block.  All operands first.
+      // key 8(r/4) + 4 half + r%4 of the block.  The operands of the first
+      // half of the k-steps first; those of the second half are read once
+      // the first two products have gone out (fewer registers held).
+      constexpr int KH = T::KS / 2;
       bf16x8 ka[T::KS], va[T::KS];
 #pragma unroll
-      for (int s = 0; s < T::KS; ++s) {
+      for (int s = 0; s < KH; ++s) {
         ka[s] = row_op<D>(kt_, lane, s);
         va[s] = row_op<D>(vt, lane, s);
       }
       f32x16 S, dP;
       mm_first(S, ka[0], qf[0]);
       mm_first(dP, va[0], df[0]);
+      {
+        const lds_char* k0 = kt_;
+        const lds_char* v0 = vt;
+        after_products(k0, v0);
+#pragma unroll
+        for (int s = KH; s < T::KS; ++s) {
+          ka[s] = row_op<D>(k0, lane, s);
+          va[s] = row_op<D>(v0, lane, s);
+        }
+      }
 #pragma unroll
       for (int s = 1; s < T::KS; ++s) {
         mm_next(S, ka[s], qf[s]);
         mm_next(dP, va[s], df[s]);
       }
-      bf16x8 tk[2][T::NDB];
+      // transposed K operands of the block's first 16 keys, read during the wait
+      bf16x8 tk[T::NDB];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int db = 0; db < T::NDB; ++db) tk[t][db] = tr_op<D>(kt_, lane, db, t);
+      for (int db = 0; db < T::NDB; ++db) tk[db] = tr_op<D>(kt_, lane, db, 0);
       pause_scores(S, dP);
       const int k0 = kb * kRows;
       const bool edge = k0 + kRows > Nk || (CAUSAL && k0 + kRows - 1 > q0w + off);
@@ -494,14 +524,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
 #pragma unroll
       for (int t = 0; t < 2; ++t) sb[t] = pack_b(dS, t);
       pause_operands(sb);
+      // the first 16 keys' products; the last 16 keys' operands are read
+      // while the second half of them runs
+      constexpr int H1 = T::NDB / 2;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int db = 0; db < H1; ++db) mm_acc(acc[db], tk[db], sb[0]);
+      const lds_char* k1 = kt_;
+      const lds_char* v1 = vt;
+      after_products(k1, v1);
+      bf16x8 uk[T::NDB];
 #pragma unroll
-        for (int db = 0; db < T::NDB; ++db) mm_acc(acc[db], tk[t][db], sb[t]);
+      for (int db = 0; db < T::NDB; ++db) uk[db] = tr_op<D>(k1, lane, db, 1);
+#pragma unroll
+      for (int db = H1; db < T::NDB; ++db) mm_acc(acc[db], tk[db], sb[0]);
+#pragma unroll
+      for (int db = 0; db < T::NDB; ++db) mm_acc(acc[db], uk[db], sb[1]);
     }
     if (kb + 1 < n_kb) {
-      sk.store(k_tile(buf ^ 1), tid);  // last read in the previous iteration
-      sv.store(v_tile(buf ^ 1), tid);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
     }
   }

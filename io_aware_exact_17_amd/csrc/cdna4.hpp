@@ -75,6 +75,25 @@ __device__ __forceinline__ float sum_row8(float x) {
   return x;
 }
 
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// One 16-byte-per-lane copy from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l's 16 bytes at gbase + voff land at LDS
+// byte lds_addr + 16 l.  Issued from inline assembly so that the compiler
+// does not tie later LDS reads to it with waits of its own: the kernel waits
+// for these copies explicitly (vmcnt, then a barrier) before reading a tile.
+__device__ __forceinline__ void copy_to_lds(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds_addr)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
 }
