@@ -321,18 +321,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       pause_scores(S, dP);
       float P[16], dS[16];
       const int key = k0w + col;
-      const bool diag = CAUSAL && k0w + kRows - 1 > qb * kRows + off;
+      // P and dS; only blocks that cross this wave's diagonal test keys
+      // (a uniform branch around vector work only: no product inside).
+      auto softmax = [&](auto masked) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < 4; ++g) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          float p = exp2_hw(S[r] * c - l4[g][i]);
-          if (diag && key > qb * kRows + 8 * g + 4 * half + i + off) p = 0.f;
-          P[r] = p;
-          dS[r] = p * (dP[r] - d4[g][i]);
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            float p = exp2_hw(S[r] * c - l4[g][i]);
+            if constexpr (decltype(masked)::value)
+              if (key > qb * kRows + 8 * g + 4 * half + i + off) p = 0.f;
+            P[r] = p;
+            dS[r] = p * (dP[r] - d4[g][i]);
+          }
         }
-      }
+      };
+      if (CAUSAL && k0w + kRows - 1 > qb * kRows + off)
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
       // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 queries.
       bf16x8 pb[2], sb[2];
 #pragma unroll
@@ -510,15 +518,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       for (int db = 0; db < T::NDB; ++db) tk[db] = tr_op<D>(kt_, lane, db, 0);
       pause_scores(S, dP);
       const int k0 = kb * kRows;
-      const bool edge = k0 + kRows > Nk || (CAUSAL && k0 + kRows - 1 > q0w + off);
       float dS[16];
+      // only blocks at the key end or across this wave's diagonal test keys
+      // (a uniform branch around vector work only: no product inside)
+      auto softmax = [&](auto masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = exp2_hw(S[r] * c - l2);
-        const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (edge && (key >= Nk || (CAUSAL && key > q + off))) p = 0.f;
-        dS[r] = p * (dP[r] - dq_row);
-      }
+        for (int r = 0; r < 16; ++r) {
+          float p = exp2_hw(S[r] * c - l2);
+          if constexpr (decltype(masked)::value) {
+            const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (key >= Nk || (CAUSAL && key > q + off)) p = 0.f;
+          }
+          dS[r] = p * (dP[r] - dq_row);
+        }
+      };
+      if (k0 + kRows > Nk || (CAUSAL && k0 + kRows - 1 > q0w + off))
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
       // dQ^T += K^T dS^T over the block's 32 keys.
       bf16x8 sb[2];
 #pragma unroll
