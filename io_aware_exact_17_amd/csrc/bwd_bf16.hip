@@ -275,14 +275,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     if (tid < 2 * kRows) reinterpret_cast<__attribute__((address_space(3))) float*>(st_tile(buf))[tid] = st;
   };
 
+  // Block qb+1 is fetched into registers during block qb-1 and written to
+  // LDS in the middle of block qb (between its last LDS reads and its
+  // softmax, when the LDS is otherwise idle); the barrier at the end of
+  // block qb publishes it.
   if (qb_first < n_qb) {
     fetch(qb_first);
     store(0);
+    if (qb_first + 1 < n_qb) fetch(qb_first + 1);
     __syncthreads();
   }
   for (int qb = qb_first; qb < n_qb; ++qb) {
     const int buf = (qb - qb_first) & 1;
-    if (qb + 1 < n_qb) fetch(qb + 1);
     {
       const lds_char* qt = q_tile(buf);
       const lds_char* dt = do_tile(buf);
@@ -319,6 +323,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         tq[db] = tr_op<D>(qt, lane, db, 0);
       }
       pause_scores(S, dP);
+      if (qb + 1 < n_qb) {
+        // buffer buf ^ 1 was last read in the previous iteration, which
+        // every wave finished before that iteration's barrier
+        store(buf ^ 1);
+        if (qb + 2 < n_qb) fetch(qb + 2);
+      }
       float P[16], dS[16];
       const int key = k0w + col;
       // P and dS; only blocks that cross this wave's diagonal test keys
@@ -377,12 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         mm_acc(dk[db], uq[db], sb[1]);
       }
     }
-    if (qb + 1 < n_qb) {
-      // buffer buf ^ 1 was last read in the previous iteration, which every
-      // wave finished before that iteration's barrier
-      store(buf ^ 1);
-      __syncthreads();
-    }
+    if (qb + 1 < n_qb) __syncthreads();
   }
 
   // dK^T / dV^T accumulators: lane = key, register r of dim block db =
