@@ -15,6 +15,8 @@ One step is one pass of the whole hot path over resident synthetic inputs:
                  gradients, by recomputation
   7. fa_fwd_block_sparse  call 1's inputs under a 64x64 block mask: a window of
                  two blocks either side of the diagonal plus the first key block
+  8. fa_fwd      GPT-2-medium-shaped attention, B=64, H=16, N=1024, d=64, bf16,
+                 non-causal, then the same inputs causal
 The batched decode streams ~8.7 GB, far more than the 256 MB last-level
 cache, so the single-request decode that follows reads its 128 MiB of K/V
 from HBM.  Every call is bracketed by HIP events on the stream it runs on.
@@ -43,9 +45,9 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBPS = 8000.0      # HBM3E
 # HBM bytes per prefill launch from rocprofv3 FETCH_SIZE + WRITE_SIZE at this
 # workload, each scaled by what the counter reads for a plain 1 GiB copy
-# (FETCH x2.0, WRITE x1.0): 231483 KiB x 2 + 66560 KiB.  Reset to None
+# (FETCH x2.0, WRITE x1.0): 242354 KiB x 2 + 66560 KiB.  Reset to None
 # whenever the prefill kernel changes until the counters are taken again.
-PREFILL_TRAFFIC_BYTES = 542234540
+PREFILL_TRAFFIC_BYTES = 564477952
 
 
 def parse():
@@ -197,6 +199,12 @@ def main():
     bs_pairs = W.block_mask_pairs(bs_mask_h[:1], P.Nq, P.Nk, True) * P.H * P.B  # same pattern per head
     bs_flops = 4.0 * P.d * bs_pairs
 
+    # GPT-2-medium-shaped attention (d = 64), non-causal and causal.
+    G = W.GPT2M
+    gq, gk, gv = W.prefill_spec_inputs(G, dev)
+    g_out = torch.empty_like(gq)
+    g_lse = torch.empty(G.B, G.H, G.Nq, dtype=torch.float32, device=dev)
+
     # A plain copy of known size, untimed: its HBM counters calibrate the
     # prefill kernel's FETCH_SIZE / WRITE_SIZE when this script runs under
     # rocprofv3 --pmc.
@@ -210,7 +218,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(rec):
-        e0, e1, e2, e3, e4, e5, e6, e7 = ev(), ev(), ev(), ev(), ev(), ev(), ev(), ev()
+        e0, e1, e2, e3, e4, e5, e6, e7, e8, e9 = (ev() for _ in range(10))
         e0.record(stream)
         fa.fa_fwd(q, k, v, P.scale, True, out=o, lse=lse)
         e1.record(stream)
@@ -231,8 +239,12 @@ def main():
         e6.record(stream)
         fa.fa_fwd_block_sparse(q, k, v, bs_mask, P.scale, True, out=bs_out, lse=bs_lse)
         e7.record(stream)
+        fa.fa_fwd(gq, gk, gv, G.scale, False, out=g_out, lse=g_lse)
+        e8.record(stream)
+        fa.fa_fwd(gq, gk, gv, G.scale, True, out=g_out, lse=g_lse)
+        e9.record(stream)
         if rec is not None:
-            rec.append((e0, e1, e2, e3, e4, e5, e6, e7))
+            rec.append((e0, e1, e2, e3, e4, e5, e6, e7, e8, e9))
 
     for _ in range(args.warmup):
         step(None)
@@ -253,6 +265,8 @@ def main():
     t_vl = [r[4].elapsed_time(r[5]) for r in recs]
     t_bw = [r[5].elapsed_time(r[6]) for r in recs]
     t_bs = [r[6].elapsed_time(r[7]) for r in recs]
+    t_gn = [r[7].elapsed_time(r[8]) for r in recs]
+    t_gc = [r[8].elapsed_time(r[9]) for r in recs]
     ms_step = wall * 1e3 / args.steps
 
     flops = P.flops()
@@ -266,6 +280,9 @@ def main():
     vl_tflops = vl_flops / (statistics.mean(t_vl) * 1e-3) / 1e12
     bw_tflops = bw_flops / (statistics.mean(t_bw) * 1e-3) / 1e12
     bs_tflops = bs_flops / (statistics.mean(t_bs) * 1e-3) / 1e12
+    g_flops, gc_flops = W.GPT2M.flops(), W.GPT2M_CAUSAL.flops()
+    gn_tflops = g_flops / (statistics.mean(t_gn) * 1e-3) / 1e12
+    gc_tflops = gc_flops / (statistics.mean(t_gc) * 1e-3) / 1e12
 
     ceil_small, ceil_big = read_ceiling(torch, fa, dev, stream, ds_bytes)
 
@@ -290,7 +307,8 @@ def main():
                         "+ the batched decode over a paged cache (16-token pages) "
                         "+ packed causal prefill 8 seqs x 32 heads d=128 len U[512,8192] "
                         "+ backward of the causal prefill + block-sparse causal prefill "
-                        "(local window of 2 blocks + first block, 64x64 blocks)",
+                        "(local window of 2 blocks + first block, 64x64 blocks) "
+                        "+ GPT-2-medium-shaped prefill B=64 H=16 N=1024 d=64, non-causal and causal",
             "prefill": {"B": P.B, "H": P.H, "Nq": P.Nq, "Nk": P.Nk, "d": P.d, "causal": True,
                         "seed": P.seed, "flops": flops, "ms_mean": round(pre_ms, 4),
                         "ms_median": round(statistics.median(t_pre), 4),
@@ -310,6 +328,10 @@ def main():
                              "ms_mean": round(statistics.mean(t_bs), 4)},
             "backward": {"B": P.B, "H": P.H, "N": P.Nq, "d": P.d, "causal": True,
                          "flops": bw_flops, "ms_mean": round(statistics.mean(t_bw), 4)},
+            "gpt2_medium": {"B": G.B, "H": G.H, "N": G.Nq, "d": G.d, "seed": G.seed,
+                            "flops_noncausal": g_flops, "flops_causal": gc_flops,
+                            "ms_mean_noncausal": round(statistics.mean(t_gn), 4),
+                            "ms_mean_causal": round(statistics.mean(t_gc), 4)},
             "prefill_varlen": {"B": VL.B, "H": VL.H, "d": VL.d, "causal": VL.causal,
                                "seed": VL.seed, "lengths": [int(x) for x in vl_lens],
                                "flops": vl_flops, "ms_mean": round(statistics.mean(t_vl), 4)},
@@ -337,6 +359,10 @@ def main():
         },
         "varlen": {"unit": "TFLOP/s", "prefill_varlen": round(vl_tflops, 2),
                    "frac_of_bf16_peak": round(vl_tflops / PEAK_BF16_TFLOPS, 4)},
+        "gpt2_medium": {"unit": "TFLOP/s", "noncausal": round(gn_tflops, 2),
+                        "causal": round(gc_tflops, 2),
+                        "frac_of_bf16_peak": {"noncausal": round(gn_tflops / PEAK_BF16_TFLOPS, 4),
+                                              "causal": round(gc_tflops / PEAK_BF16_TFLOPS, 4)}},
         "block_sparse": {"unit": "TFLOP/s", "value": round(bs_tflops, 2),
                          "flops_convention": "4 * d * visible (query, key) pairs"},
         "backward": {"unit": "TFLOP/s", "value": round(bw_tflops, 2),
