@@ -88,15 +88,25 @@ __device__ __forceinline__ int vt_pos4(int group4) {
   return ((group4 & 1) << 1) | ((group4 >> 1) & 1);
 }
 
+// The work is a list of items, one per (sequence or batch-head, query tile),
+// heaviest query tile first and heads fastest.  Workgroup g takes items g,
+// g + G, g + 2G, ... (G = number of workgroups) and walks them as one stream
+// of positions, one per key tile of each item in turn (an item with no
+// visible key still takes one position, for its epilogue).  The staging of
+// tiles two positions ahead, the lag of wave group B and the fetch of the
+// next item's Q all run across item boundaries, so a workgroup pays for the
+// pipeline's fill and drain once, not once per query tile.
+//
 // VARLEN: a packed batch of sequences (token-major [T, H, d], sequence b owns
 // query rows cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1, LSE
-// [H, total_q], grid (the longest sequence's query tiles x H, B)); otherwise
-// dense [B, H, N, d].
+// [H, total_q]); items run sequence by sequence (the longest sequence's query
+// tiles x H per sequence), and items past a sequence's last query tile are
+// empty and skipped.  Otherwise dense [B, H, N, d].
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int Nq_dense, int Nk_dense,
-    float c, int negate_q, int n_qtiles, const int32_t* __restrict__ cu_q,
+    float c, int negate_q, int n_qtiles, int n_items, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int H, int total_q) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
@@ -110,58 +120,95 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const bool group_b = wave >= 4;
   const int col = lane & 31;   // query column of this lane in S^T / O^T
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group this lane holds
-
-  // Heaviest query tile first; heads vary fastest.
-  int qt, Nq, Nk;
-  size_t qbase, kbase, lse_base;  // elements
-  if constexpr (VARLEN) {
-    // One sequence after another (grid.y), so the workgroups running
-    // together share that sequence's K/V in L2; within it, heaviest tile
-    // first, heads fastest.
-    const int h = (int)(blockIdx.x % H);
-    const int b = (int)blockIdx.y;
-    qt = n_qtiles - 1 - (int)(blockIdx.x / H);
-    const int qs = cu_q[b], ks = cu_k[b];
-    Nq = cu_q[b + 1] - qs;
-    Nk = cu_k[b + 1] - ks;
-    if (qt * kBR >= Nq) return;  // past this sequence's last query tile
-    qbase = ((size_t)qs * H + h) * D;
-    kbase = ((size_t)ks * H + h) * D;
-    lse_base = (size_t)h * total_q + qs;
-  } else {
-    qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
-    const int bh = (int)(blockIdx.x % BH);
-    Nq = Nq_dense;
-    Nk = Nk_dense;
-    qbase = (size_t)bh * Nq * D;
-    kbase = (size_t)bh * Nk * D;
-    lse_base = (size_t)bh * Nq;
-  }
+  const int G = (int)gridDim.x;
   const int rs = VARLEN ? H * D : D;  // elements between consecutive rows of a head
-  const int q0 = qt * kBR;
-  const int off = Nk - Nq;  // bottom-right causal alignment
 
-  const int kv_end = CAUSAL ? min(Nk, q0 + kBR + off) : Nk;
-  const int n_tiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  // ------------------------------------------------------------- the items
+  struct Item {
+    int Nq, Nk, q0, n_tiles;
+    size_t qbase, kbase, lse_base;  // elements
+  };
+  // Returns false for an empty item (a query tile past its sequence's end).
+  auto item_info = [&](int i, Item& it) -> bool {
+    int qt;
+    if constexpr (VARLEN) {
+      const int per = n_qtiles * H;
+      const int b = i / per, r = i - b * per;
+      const int h = r % H;
+      qt = n_qtiles - 1 - r / H;
+      const int qs = cu_q[b], ks = cu_k[b];
+      it.Nq = cu_q[b + 1] - qs;
+      it.Nk = cu_k[b + 1] - ks;
+      if (qt * kBR >= it.Nq) return false;
+      it.qbase = ((size_t)qs * H + h) * D;
+      it.kbase = ((size_t)ks * H + h) * D;
+      it.lse_base = (size_t)h * total_q + qs;
+    } else {
+      qt = n_qtiles - 1 - i / BH;
+      const int bh = i % BH;
+      it.Nq = Nq_dense;
+      it.Nk = Nk_dense;
+      it.qbase = (size_t)bh * it.Nq * D;
+      it.kbase = (size_t)bh * it.Nk * D;
+      it.lse_base = (size_t)bh * it.Nq;
+    }
+    it.q0 = qt * kBR;
+    const int kv_end = CAUSAL ? min(it.Nk, it.q0 + kBR + it.Nk - it.Nq) : it.Nk;
+    it.n_tiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+    return true;
+  };
+  // Key tiles this wave's 32 rows need (causal: up to its last row's diagonal).
+  auto tiles_of_wave = [&](const Item& it) -> int {
+    const int end = CAUSAL ? min(it.Nk, it.q0 + wave * 32 + 32 + it.Nk - it.Nq) : it.Nk;
+    return end > 0 ? (end + BC - 1) / BC : 0;
+  };
+  // A stream position: key tile j of this workgroup's item `item`, which
+  // spans n_pos = max(n_tiles, 1) positions.  item >= n_items ends the stream.
+  struct Cursor {
+    int item, j, n_pos;
+    Item it;  // the item's description (valid while item < n_items)
+  };
+  auto settle = [&](Cursor& cu) {  // move to the first non-empty item at or after cu.item
+    while (cu.item < n_items && !item_info(cu.item, cu.it)) cu.item += G;
+    cu.j = 0;
+    cu.n_pos = cu.item < n_items ? max(cu.it.n_tiles, 1) : 0;
+  };
+  auto advance = [&](Cursor& cu) {
+    if (++cu.j < cu.n_pos) return;
+    cu.item += G;
+    settle(cu);
+  };
 
-  const int wq0 = q0 + wave * 32;  // first query row of this wave
-  const int qi = wq0 + col;        // this lane's query row
-  const int kv_end_w = CAUSAL ? min(Nk, wq0 + 32 + off) : Nk;
-  const int nt_w = kv_end_w > 0 ? (kv_end_w + BC - 1) / BC : 0;  // tiles this wave needs
+  Cursor cur;
+  cur.item = (int)blockIdx.x;
+  settle(cur);
+  if (cur.item >= n_items) return;  // uniform: no work for this workgroup
 
   // Q^T operand: lane holds Q[qi][16s + 8*half + 0..7].  Rows past Nq read
   // row Nq-1 (their results are never stored).
-  bf16x8 qf[C::KS];
-  {
-    const uint32_t flip = negate_q ? 0x80008000u : 0u;  // exact sign flip for a negative scale
-    const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)min(qi, Nq - 1) * rs);
+  const uint32_t flip = negate_q ? 0x80008000u : 0u;  // exact sign flip for a negative scale
+  auto load_q = [&](const Item& it, u32x4 (&dst)[C::KS]) {
+    const int qi = it.q0 + wave * 32 + col;
+    const u32x4* src = reinterpret_cast<const u32x4*>(Q + it.qbase + (size_t)min(qi, it.Nq - 1) * rs);
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      u32x4 w = src[2 * s + half];
-      w ^= flip;
-      qf[s] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
+    for (int s = 0; s < C::KS; ++s) dst[s] = src[2 * s + half];
+  };
+  bf16x8 qf[C::KS];
+  u32x4 qn[C::KS];  // the next item's Q, fetched one position ahead
+  auto take_q = [&]() {
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qn[s] ^ flip);
+  };
+  load_q(cur.it, qn);
+  take_q();
+  // At the last position of an item, fetch the next item's Q into qn.
+  auto prefetch_q = [&](const Cursor& cu) {
+    if (cu.j != cu.n_pos - 1) return;
+    Cursor nx;
+    nx.item = cu.item + G;
+    settle(nx);
+    if (nx.item < n_items) load_q(nx.it, qn);
+  };
 
   // ---------------------------------------------------------- tile staging
   // Waves 0-3 move V, waves 4-7 move K, four 16-byte chunks per thread.
@@ -169,6 +216,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   //     mt / (D/8) + (256 / (D/8)) i, 8 dims at (mt % (D/8)) * 8.
   //   V mover mt: keys 4*vkg .. 4*vkg+3 of dims vdb*8 .. vdb*8+7, written to
   //     V^T transposed.
+  // Position p of the stream uses K buffer p % kKBuf and V^T buffer p % kVBuf.
   const bool k_mover = tid >= kMovers;
   const int mt = tid & (kMovers - 1);
   constexpr int kKeysPerPass = kMovers / (D / 8);
@@ -181,25 +229,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   // The tile base is uniform, so loads take an SGPR base plus a 32-bit lane
   // byte offset.  Keys past Nk read row Nk-1 instead: finite values whose
-  // scores are masked to -inf, so they carry zero weight.
-  auto load_tile = [&](int j) {
-    const int k0 = j * BC;
-    const char* base = reinterpret_cast<const char*>((k_mover ? K : V) + kbase + (size_t)k0 * rs);
-    const int last = Nk - 1 - k0;
+  // scores are masked to -inf, so they carry zero weight.  A position with
+  // no key tile (an item with no visible key) loads nothing.
+  auto load_tile = [&](const Cursor& cu) {
+    const Item& it = cu.it;
+    if (it.n_tiles == 0) return;
+    const int k0 = cu.j * BC;
+    const char* base = reinterpret_cast<const char*>((k_mover ? K : V) + it.kbase + (size_t)k0 * rs);
+    const int last = it.Nk - 1 - k0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = min(first_key + key_step * i, last);
       stg[i] = *reinterpret_cast<const u32x4*>(base + (uint32_t)((key * rs + dcol) * 2));
     }
   };
-  auto store_tile = [&](int j) {
+  auto store_tile = [&](int p) {
     if (k_mover) {
-      bf16* sk = sK + (j % kKBuf) * C::KTILE;
+      bf16* sk = sK + (p % kKBuf) * C::KTILE;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x4*>(sk + (first_key + key_step * i) * C::KROW + dcol) = stg[i];
     } else {
-      bf16* sv = sV + (j % kVBuf) * C::VTILE;
+      bf16* sv = sV + (p % kVBuf) * C::VTILE;
       // 4 keys x 8 dims -> 8 rows of V^T, 4 keys each.
       const int pos = 16 * (vkg >> 2) + 4 * vt_pos4(vkg & 3);
 #pragma unroll
@@ -239,9 +290,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   // The wave feeding the matrix core runs at raised issue priority, so the
   // neighbouring wave's vector work fills the gaps instead of delaying it.
-  auto qk = [&](int j) {
+  auto qk = [&](int p) {
     __builtin_amdgcn_s_setprio(1);
-    const bf16* sk = sK + (j % kKBuf) * C::KTILE + col * C::KROW + half * 8;
+    const bf16* sk = sK + (p % kKBuf) * C::KTILE + col * C::KROW + half * 8;
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
@@ -255,9 +306,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     __builtin_amdgcn_s_setprio(0);
   };
 
-  auto pv = [&](int j) {
+  auto pv = [&](int p) {
     __builtin_amdgcn_s_setprio(1);
-    const bf16* sv = sV + (j % kVBuf) * C::VTILE + col * C::VROW + half * 8;
+    const bf16* sv = sV + (p % kVBuf) * C::VTILE + col * C::VROW + half * 8;
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -293,12 +344,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         pk[kb][r >> 1] = pack_bf16x2(p0, p1);
       }
   };
-  auto softmax = [&](int j) {
+  auto softmax = [&](const Item& it, int j) {
     const int k0 = j * BC;
-    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wq0 + off);
+    const int off = it.Nk - it.Nq;  // bottom-right causal alignment
+    const int wq0 = it.q0 + wave * 32;
+    const bool need_mask = (k0 + BC > it.Nk) || (CAUSAL && k0 + BC - 1 > wq0 + off);
     if (__builtin_expect(need_mask, 0)) {
       [[unlikely]];
-      const int lim = CAUSAL ? min(Nk - 1, qi + off) : Nk - 1;
+      const int lim = CAUSAL ? min(it.Nk - 1, wq0 + col + off) : it.Nk - 1;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -330,51 +383,87 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     l_part += lsum;
   };
 
+  // One division per row, O in bf16, LSE = ln2 * (m + log2 l); then the
+  // running state starts again for the next item.
+  auto epilogue = [&](const Item& it) {
+    const int qi = it.q0 + wave * 32 + col;
+    const float l_tot = sum_across_halves(l_part);
+    if (qi < it.Nq) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      bf16* orow = O + it.qbase + (size_t)qi * rs;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                           pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * half) = w;
+        }
+      if (half == 0)
+        LSE[it.lse_base + qi] = l_tot > 0.f ? (m_ref + log2_hw(l_tot)) * kLn2 : kNegInf;
+    }
+#pragma unroll
+    for (int i = 0; i < C::NDB; ++i) oacc[i] = f32x16{};
+    m_ref = kNegInf;
+    l_part = 0.f;
+  };
+
   // ------------------------------------------------------------- main loop
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (n_tiles > 1) load_tile(1);
-  }
+  // Position 0 is staged and position 1 fetched before the first barrier;
+  // `ld` is the position whose tile the staging registers hold or will hold.
+  Cursor ld = cur;
+  load_tile(ld);
+  store_tile(0);
+  advance(ld);
+  if (ld.item < n_items) load_tile(ld);
   __syncthreads();
 
-  // Group B finishes the previous tile's P V first, so it runs one extra
-  // iteration after the last tile.
-  for (int j = 0; j <= n_tiles; ++j) {
+  // Group B finishes the previous position's P V first, so the stream ends
+  // with one extra step in which only group B works.
+  Cursor prv;  // the position before cur (none yet)
+  prv.item = n_items;
+  for (int p = 0; cur.item < n_items || prv.item < n_items; ++p) {
+    const bool have_cur = cur.item < n_items;
+    const Item& ic = cur.it;
     if (!group_b) {
-      if (j < nt_w) {
-        qk(j);
-        softmax(j);
-        pv(j);
+      if (have_cur) {
+        prefetch_q(cur);
+        if (cur.j < tiles_of_wave(ic)) {
+          qk(p);
+          softmax(ic, cur.j);
+          pv(p);
+        }
+        if (cur.j == cur.n_pos - 1) {
+          epilogue(ic);
+          take_q();
+        }
       }
     } else {
-      if (j >= 1 && j - 1 < nt_w) pv(j - 1);
-      if (j < nt_w) {
-        qk(j);
-        softmax(j);
+      if (prv.item < n_items) {
+        const Item& ip = prv.it;
+        if (prv.j < tiles_of_wave(ip)) pv(p - 1);
+        if (prv.j == prv.n_pos - 1) {
+          epilogue(ip);
+          if (have_cur) take_q();
+        }
+      }
+      if (have_cur) {
+        prefetch_q(cur);
+        if (cur.j < tiles_of_wave(ic)) {
+          qk(p);
+          softmax(ic, cur.j);
+        }
       }
     }
-    // Stage tile j+1 (loaded one iteration ago) and fetch tile j+2.
-    if (j + 1 < n_tiles) store_tile(j + 1);
-    if (j + 2 < n_tiles) load_tile(j + 2);
+    // Stage position p+1 (fetched one step ago) and fetch position p+2.
+    if (ld.item < n_items) {
+      store_tile(p + 1);
+      advance(ld);
+      if (ld.item < n_items) load_tile(ld);
+    }
     __syncthreads();
-  }
-
-  // Epilogue: one division per row, O in bf16, LSE = ln2 * (m + log2 l).
-  const float l_tot = sum_across_halves(l_part);
-  if (qi < Nq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16* orow = O + qbase + (size_t)qi * rs;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                         pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * half) = w;
-      }
-    if (half == 0)
-      LSE[lse_base + qi] = l_tot > 0.f ? (m_ref + log2_hw(l_tot)) * kLn2 : kNegInf;
+    prv = cur;
+    if (have_cur) advance(cur);
   }
 }
 
@@ -387,13 +476,25 @@ hipError_t launch(const FwdArgs& a) {
   // against the reference, so the weights are exactly uniform, as for 0.
   const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   const int neg = a.scale < 0.f ? 1 : 0;
-  const dim3 grid = VARLEN ? dim3((unsigned)(n_qtiles * a.H), (unsigned)a.B)
-                           : dim3((unsigned)(n_qtiles * BH));
+  const int n_items = n_qtiles * BH;
+  // Dense: one workgroup per CU (the LDS and registers of one workgroup fill
+  // a CU), each walking every G-th item; the items alternate over the heads,
+  // so with B*H a multiple of 8 a head's items stay on one XCD.  Varlen: one
+  // workgroup per item, so the hardware balances sequences of any length.
+  int G = n_items;
+  if constexpr (!VARLEN) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    G = min(n_items, max(cus, 1));
+  }
+  const dim3 grid((unsigned)G);
   const dim3 block(kThreads);
-  void* args[] = {(void*)&a.q,    (void*)&a.k,        (void*)&a.v,    (void*)&a.o,
-                  (void*)&a.lse,  (void*)&BH,         (void*)&a.Nq,   (void*)&a.Nk,
-                  (void*)&c,      (void*)&neg,        (void*)&n_qtiles, (void*)&a.cu_q,
-                  (void*)&a.cu_k, (void*)&a.H,        (void*)&a.total_q};
+  void* args[] = {(void*)&a.q,    (void*)&a.k,   (void*)&a.v,        (void*)&a.o,
+                  (void*)&a.lse,  (void*)&BH,    (void*)&a.Nq,       (void*)&a.Nk,
+                  (void*)&c,      (void*)&neg,   (void*)&n_qtiles,   (void*)&n_items,
+                  (void*)&a.cu_q, (void*)&a.cu_k, (void*)&a.H,       (void*)&a.total_q};
   return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL, VARLEN>), grid,
                          block, args, 0, a.stream);
 }

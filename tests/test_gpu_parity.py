@@ -253,6 +253,7 @@ VARLEN_CASES = [
     (128, False, [513, 7, 64], [1025, 33, 64]),
     (64, True, [1, 129, 500], [1, 700, 500]),
     (64, False, [200, 40], [77, 3000]),
+    (64, True, [300, 0, 70, 5], [64, 5, 0, 700]),     # empty sequence, keyless rows
 ]
 
 
@@ -281,6 +282,34 @@ def test_fwd_varlen_equals_dense(fa, d, causal):
     torch.cuda.synchronize()
     assert torch.equal(pack(o), o2)
     assert torch.equal(lse.permute(1, 0, 2).reshape(H, B * N), lse2)
+
+
+# d = 64 runs as a stream: one workgroup per CU walks every G-th query tile
+# (G = CU count), carrying its tile pipeline across query tiles.  These shapes
+# have more query tiles than CUs, mixed tile counts and, causally with
+# Nq > Nk, query tiles that see no key at all.
+D64_STREAM = [
+    # B, H, Nq, Nk, causal
+    (1, 128, 600, 100, True),
+    (2, 100, 300, 333, False),
+    (1, 96, 1000, 1000, True),
+]
+
+
+@pytest.mark.parametrize("shape", D64_STREAM, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_d64_stream(fa, shape):
+    B, H, Nq, Nk, causal = shape
+    log(f"case d64 stream {shape}")
+    q, k, v = W.prefill_inputs(B, H, Nq, Nk, 64, "bf16", seed=Nq + Nk + H, device="cuda")
+    o, lse = run_fwd(fa, q, k, v, 0.125, causal)
+    O, L = oracle.attention(q, k, v, 0.125, causal)
+    check(o, lse, O, L, TOL_BF16, f"d64 stream {shape}")
+    # A head computed alone (one query tile per workgroup) is bit-identical
+    # to the same head inside the stream: nothing carries over between tiles.
+    for b, h in [(0, 0), (B - 1, H // 2), (B - 1, H - 1)]:
+        o1, lse1 = run_fwd(fa, q[b:b + 1, h:h + 1].contiguous(), k[b:b + 1, h:h + 1].contiguous(),
+                           v[b:b + 1, h:h + 1].contiguous(), 0.125, causal)
+        assert torch.equal(o1[0, 0], o[b, h]) and torch.equal(lse1[0, 0], lse[b, h]), (b, h)
 
 
 def test_fwd_varlen_full_size_sampled(fa):
