@@ -329,9 +329,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // then P = 2^(s*c - m) against the current reference m, the row sum and
   // the bf16 pairs of P.  The reference only has to keep every P small, so
   // instead of a row maximum per tile the tile's own sum decides: if any
-  // lane's share exceeds 2^tau (or is not finite: m = -inf before the first
-  // visible key), the wave takes the exact path once — row maximum, new
-  // reference, O and l rescaled, P recomputed.  Either way every P <= 2^tau.
+  // lane's share exceeds 2^tau, or some row has no reference yet, the wave
+  // takes the exact path — row maximum, new reference, O and l rescaled, P
+  // formed from the new reference.  Either way every P <= 2^tau.
   auto exp_tile = [&](float m_use, float& lsum) {
     lsum = 0.f;
 #pragma unroll
@@ -360,9 +360,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           if (key > lim) sacc[kb][r] = kNegInf;
         }
     }
-    float lsum;
-    exp_tile(m_ref, lsum);  // m_ref = -inf gives +inf/NaN sums, caught below
-    if (__builtin_expect(wave_any(!(lsum <= kSumBound)), 0)) {
+    // Until a row has a reference (m_ref = -inf: its first tile with a
+    // visible key) the wave goes straight to the exact path; otherwise it
+    // takes the exact path only when the tile's sum bound fails.
+    float lsum = 0.f;
+    bool exact = wave_any(m_ref == kNegInf);
+    if (__builtin_expect(!exact, 1)) {
+      exp_tile(m_ref, lsum);
+      exact = wave_any(!(lsum <= kSumBound));
+    }
+    if (__builtin_expect(exact, 0)) {
       [[unlikely]];
       float mx = kNegInf;
 #pragma unroll
