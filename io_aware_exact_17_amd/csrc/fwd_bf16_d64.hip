@@ -44,10 +44,12 @@
 //    taken, the reference moved and the output accumulator rescaled.  That
 //    happens on the first tile and rarely afterwards; the mathematics is
 //    unchanged because the final division uses the same reference.
-//  * Workgroups are issued heaviest query tile first; consecutive workgroup
-//    ids walk the heads, so when B*H is a multiple of 8 every tile of a head
-//    lands on the same XCD (workgroups are dealt round-robin to the 8 XCDs)
-//    and shares its K/V in that XCD's L2.
+//  * Work items (head, query tile) are listed heaviest query tile first,
+//    heads fastest.  Dense runs one workgroup per CU, each walking every
+//    G-th item as one stream (see the kernel); since workgroups are dealt
+//    round-robin to the 8 XCDs and G is a multiple of 8, with B*H a multiple
+//    of 8 every item of a head lands on the same XCD and shares its K/V in
+//    that XCD's L2.
 #include "cdna4.hpp"
 #include "kernels.hpp"
 
