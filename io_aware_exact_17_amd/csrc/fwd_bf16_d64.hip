@@ -47,9 +47,9 @@
 //  * Work items (head, query tile) are listed heaviest query tile first,
 //    heads fastest.  Dense runs one workgroup per CU, each walking every
 //    G-th item as one stream (see the kernel); since workgroups are dealt
-//    round-robin to the 8 XCDs and G is a multiple of 8, with B*H a multiple
-//    of 8 every item of a head lands on the same XCD and shares its K/V in
-//    that XCD's L2.
+//    round-robin to the 8 XCDs, when G (the CU count, 256, once there are
+//    that many items) and B*H are multiples of 8 every item of a head lands
+//    on the same XCD and shares its K/V in that XCD's L2.
 #include "cdna4.hpp"
 #include "kernels.hpp"
 
