@@ -99,8 +99,10 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   if (max_seqlen_q > total_q) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  // grid = (query tiles of the longest sequence x H, B), same tile height as dense
-  if (fa::fwd_bf16_grid(1, H, max_seqlen_q) > kMaxGridX) return FA_ERR_INVALID_ARG;
+  // d = 128: grid = (query tiles of the longest sequence x H, B); d = 64: one
+  // workgroup per (sequence, query tile, head) item, counted over the whole
+  // batch.  Same tile height as dense.
+  if (fa::fwd_bf16_grid(d == 64 ? B : 1, H, max_seqlen_q) > kMaxGridX) return FA_ERR_INVALID_ARG;
   fa::FwdArgs a{q, k, v, o, lse, B, H, max_seqlen_q, 0, d, scale, causal ? 1 : 0, stream};
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;

@@ -79,6 +79,28 @@ def test_fwd_rejects_invalid_arguments(entry):
     assert fwd_call(entry, B=65535, H=65535 // 2, Nq=1 << 20) == INVALID
 
 
+def varlen_call(q=A, k=A, v=A, o=A2, lse=A2, cq=A2, ck=A2, B=2, H=4, d=64, total_q=100,
+                max_seqlen_q=60, scale=0.125, causal=1):
+    lib = fa.load()
+    return lib.fa_fwd_varlen(q, k, v, o, lse, cq, ck, B, H, d, total_q, max_seqlen_q, scale,
+                             causal, None)
+
+
+def test_varlen_rejects_bad_arguments():
+    for kw in ("q", "k", "v", "o", "lse", "cq", "ck"):
+        assert varlen_call(**{kw: None}) == INVALID
+    assert varlen_call(q=A + 8) == INVALID
+    assert varlen_call(cq=A2 + 2) == INVALID
+    for bad in ({"B": 0}, {"B": 65536}, {"H": 0}, {"total_q": 0}, {"max_seqlen_q": 0},
+                {"max_seqlen_q": 101}, {"scale": float("nan")}):
+        assert varlen_call(**bad) == INVALID
+    for d in (0, 32, 96, 256):
+        assert varlen_call(d=d) == UNSUPPORTED
+    # d = 64 counts one workgroup per (sequence, query tile, head) over the
+    # whole batch: 600 tiles x 65535 sequences x 64 heads > 2^31 - 1.
+    assert varlen_call(B=65535, H=64, total_q=600 * 256, max_seqlen_q=600 * 256) == INVALID
+
+
 def dec_call(q=A, kc=A, vc=A, sl=A2, off=A2, o=A2, lse=A2, B=2, H=4, d=128, max_seqlen=100,
              scale=0.1, split_keys=0, ws=A, ws_bytes=1 << 30):
     lib = fa.load()
