@@ -130,9 +130,9 @@ def test_workspace_and_split_plan():
     # a single long sequence is cut into 256-key chunks
     assert fa.fa_decode_split_keys(1, 32, 128, 8192) == 256
     assert fa.fa_decode_workspace_bytes(1, 32, 128, 8192, 0) == 1 * 32 * 32 * 130 * 4
-    # a large batch gets longer chunks, keeping the grid <= 32768 workgroups
+    # a large batch gets longer chunks, keeping the grid <= 16384 workgroups
     sk = fa.fa_decode_split_keys(64, 32, 128, 16384)
-    assert sk % 64 == 0 and 64 * 32 * -(-16384 // sk) <= 32768
+    assert sk == 2048 and 64 * 32 * -(-16384 // sk) <= 16384
     assert fa.fa_decode_workspace_bytes(3, 5, 64, 1000, 128) == 3 * 5 * 8 * 66 * 4
     # at most 256 chunks per sequence
     assert -(-(1 << 24) // fa.fa_decode_split_keys(1, 1, 128, 1 << 24)) <= 256
