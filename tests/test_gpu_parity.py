@@ -124,12 +124,16 @@ def test_edge_shapes(fa, shape, dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
-def test_unusual_scales(fa, dtype, scale):
-    log(f"case scale {scale} {dtype}")
-    q, k, v = W.prefill_inputs(1, 2, 150, 170, 128, dtype, seed=5, device="cuda")
+@pytest.mark.parametrize("d", [64, 128])
+def test_unusual_scales(fa, dtype, scale, d):
+    log(f"case scale {scale} {dtype} d={d}")
+    # bf16 d = 64 with 200 heads x 2 query tiles: more tiles than CUs, so the
+    # sign flip and the zero-scale path also run inside a stream of tiles.
+    H, Nq = (200, 300) if (d == 64 and dtype == "bf16") else (2, 150)
+    q, k, v = W.prefill_inputs(1, H, Nq, 170, d, dtype, seed=5 + d, device="cuda")
     o, lse = run_fwd(fa, q, k, v, scale, True)
     O, L = oracle.attention(q, k, v, scale, True)
-    check(o, lse, O, L, TOL_F32 if dtype == "f32" else TOL_BF16, f"scale={scale} {dtype}")
+    check(o, lse, O, L, TOL_F32 if dtype == "f32" else TOL_BF16, f"scale={scale} {dtype} d={d}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
