@@ -30,7 +30,8 @@
  * Ownership and threading.  The caller allocates and owns every buffer
  * (inputs, outputs, workspace) and picks the stream.  The library allocates
  * no device memory, keeps no pointer after a call returns and holds no
- * mutable global state; calls are thread-safe.
+ * mutable global state beyond a cache of each device's compute-unit count
+ * (read on first use, never changed after); calls are thread-safe.
  *
  * Alignment.  q, k, v, o, kcache, vcache and the workspace must be 16-byte
  * aligned; lse, seqlens, offsets and the decode output 4-byte aligned

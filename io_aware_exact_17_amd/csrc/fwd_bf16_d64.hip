@@ -50,6 +50,8 @@
 //    round-robin to the 8 XCDs, when G (the CU count, 256, once there are
 //    that many items) and B*H are multiples of 8 every item of a head lands
 //    on the same XCD and shares its K/V in that XCD's L2.
+#include <atomic>
+
 #include "cdna4.hpp"
 #include "kernels.hpp"
 
@@ -64,6 +66,7 @@ constexpr int kKBuf = 2;          // LDS K buffers
 constexpr int kVBuf = 3;          // LDS V^T buffers
 constexpr float kSumBound = 256.f;  // a tile's P sum per lane half stays <= 2^8
 constexpr int kPrefetch = 6;      // LDS operand reads kept ahead of the matrix cores
+constexpr int kMaxDevices = 64;   // devices whose CU count is cached
 
 template <int D>
 struct FwdCfg {
@@ -476,6 +479,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   }
 }
 
+// Compute units of the device `stream` belongs to (the null stream: the
+// current device), read once per device and kept: a device property, not
+// state that changes between calls.
+hipError_t cu_count(hipStream_t stream, int* cus) {
+  static std::atomic<int> cache[kMaxDevices];
+  hipDevice_t dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n <= 0) return hipErrorInvalidDevice;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  *cus = n;
+  return hipSuccess;
+}
+
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdArgs& a) {
   const int n_qtiles = (a.Nq + kBR - 1) / kBR;
@@ -492,11 +515,10 @@ hipError_t launch(const FwdArgs& a) {
   // workgroup per item, so the hardware balances sequences of any length.
   int G = n_items;
   if constexpr (!VARLEN) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipErrorInvalidDevice;
-    G = min(n_items, max(cus, 1));
+    int cus = 0;
+    const hipError_t e = cu_count(a.stream, &cus);
+    if (e != hipSuccess) return e;
+    G = min(n_items, cus);
   }
   const dim3 grid((unsigned)G);
   const dim3 block(kThreads);
