@@ -244,6 +244,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int qi0 = wq0 + col;       // this lane's row in row block 0 (+32 in block 1)
   const int kv_end_w = CAUSAL ? min(Nk, wq0 + 64 + off) : Nk;
 
+  // Q^T operands: lane holds Q[row][16s + 8*half + 0..7] of both row blocks.
+  // Rows past Nq read row Nq-1 (their results are never stored).
+  // They are loaded straight into accumulation registers, where only the
+  // S^T products read them; the first wait on vector memory (the block mask
+  // read below, or the wait before the first barrier) covers these loads,
+  // which are issued first so that their latency overlaps the mask read.
+  bf16x8 qf[2][C::KS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const bf16* src = Q + qbase + (size_t)min(qi0 + 32 * rb, Nq - 1) * q_rs + 8 * half;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) qf[rb][s] = load_to_acc(src + 16 * s);
+  }
+
   // Block-sparse: the list of key tiles (s_tile) that any of the four mask
   // rows of the workgroup admits, in order, with the admitting waves as bits
   // (s_vis); compacted with one ballot per wave and 256 candidates per pass.
@@ -311,19 +325,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     else
       return true;
   };
-
-  // Q^T operands: lane holds Q[row][16s + 8*half + 0..7] of both row blocks.
-  // Rows past Nq read row Nq-1 (their results are never stored).
-  // They are loaded straight into accumulation registers, where only the
-  // S^T products read them; the first wait on vector memory (before the
-  // first barrier) covers these loads.
-  bf16x8 qf[2][C::KS];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const bf16* src = Q + qbase + (size_t)min(qi0 + 32 * rb, Nq - 1) * q_rs + 8 * half;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) qf[rb][s] = load_to_acc(src + 16 * s);
-  }
 
   // ---------------------------------------------------------- tile staging
   // Wave w issues wave instructions w*IPW .. w*IPW+IPW-1 of a tile; wave
