@@ -129,42 +129,64 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int rs = VARLEN ? H * D : D;  // elements between consecutive rows of a head
 
   // ------------------------------------------------------------- the items
+  // An item is kept as a few integers; row bases, lengths and tile counts
+  // are derived on use (dense: from the kernel arguments), which keeps the
+  // three cursors below within the scalar registers.
   struct Item {
-    int Nq, Nk, q0, n_tiles;
-    size_t qbase, kbase, lse_base;  // elements
+    int qt;      // query tile
+    int bh;      // batch-head (dense) or head (varlen)
+    int qs, ks;  // varlen: the sequence's first query and key rows
+    int nq, nk;  // varlen: the sequence's query and key counts
+  };
+  auto Nq_of = [&](const Item& it) -> int {
+    if constexpr (VARLEN) return it.nq;
+    else return Nq_dense;
+  };
+  auto Nk_of = [&](const Item& it) -> int {
+    if constexpr (VARLEN) return it.nk;
+    else return Nk_dense;
+  };
+  auto q0_of = [&](const Item& it) -> int { return it.qt * kBR; };
+  auto qbase_of = [&](const Item& it) -> size_t {  // elements
+    if constexpr (VARLEN) return ((size_t)it.qs * H + it.bh) * D;
+    else return (size_t)it.bh * Nq_dense * D;
+  };
+  auto kbase_of = [&](const Item& it) -> size_t {
+    if constexpr (VARLEN) return ((size_t)it.ks * H + it.bh) * D;
+    else return (size_t)it.bh * Nk_dense * D;
+  };
+  auto lse_base_of = [&](const Item& it) -> size_t {
+    if constexpr (VARLEN) return (size_t)it.bh * total_q + it.qs;
+    else return (size_t)it.bh * Nq_dense;
+  };
+  // Key tiles of the item (causal: up to the diagonal of its last row).
+  auto n_tiles_of = [&](const Item& it) -> int {
+    const int Nk = Nk_of(it);
+    const int kv_end = CAUSAL ? min(Nk, q0_of(it) + kBR + Nk - Nq_of(it)) : Nk;
+    return kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
   };
   // Returns false for an empty item (a query tile past its sequence's end).
   auto item_info = [&](int i, Item& it) -> bool {
-    int qt;
     if constexpr (VARLEN) {
       const int per = n_qtiles * H;
       const int b = i / per, r = i - b * per;
-      const int h = r % H;
-      qt = n_qtiles - 1 - r / H;
-      const int qs = cu_q[b], ks = cu_k[b];
-      it.Nq = cu_q[b + 1] - qs;
-      it.Nk = cu_k[b + 1] - ks;
-      if (qt * kBR >= it.Nq) return false;
-      it.qbase = ((size_t)qs * H + h) * D;
-      it.kbase = ((size_t)ks * H + h) * D;
-      it.lse_base = (size_t)h * total_q + qs;
+      it.bh = r % H;
+      it.qt = n_qtiles - 1 - r / H;
+      it.qs = cu_q[b];
+      it.ks = cu_k[b];
+      it.nq = cu_q[b + 1] - it.qs;
+      it.nk = cu_k[b + 1] - it.ks;
+      return it.qt * kBR < it.nq;
     } else {
-      qt = n_qtiles - 1 - i / BH;
-      const int bh = i % BH;
-      it.Nq = Nq_dense;
-      it.Nk = Nk_dense;
-      it.qbase = (size_t)bh * it.Nq * D;
-      it.kbase = (size_t)bh * it.Nk * D;
-      it.lse_base = (size_t)bh * it.Nq;
+      it.qt = n_qtiles - 1 - i / BH;
+      it.bh = i % BH;
+      return true;
     }
-    it.q0 = qt * kBR;
-    const int kv_end = CAUSAL ? min(it.Nk, it.q0 + kBR + it.Nk - it.Nq) : it.Nk;
-    it.n_tiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
-    return true;
   };
   // Key tiles this wave's 32 rows need (causal: up to its last row's diagonal).
   auto tiles_of_wave = [&](const Item& it) -> int {
-    const int end = CAUSAL ? min(it.Nk, it.q0 + wave * 32 + 32 + it.Nk - it.Nq) : it.Nk;
+    const int Nk = Nk_of(it);
+    const int end = CAUSAL ? min(Nk, q0_of(it) + wave * 32 + 32 + Nk - Nq_of(it)) : Nk;
     return end > 0 ? (end + BC - 1) / BC : 0;
   };
   // A stream position: key tile j of this workgroup's item `item`, which
@@ -176,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   auto settle = [&](Cursor& cu) {  // move to the first non-empty item at or after cu.item
     while (cu.item < n_items && !item_info(cu.item, cu.it)) cu.item += G;
     cu.j = 0;
-    cu.n_pos = cu.item < n_items ? max(cu.it.n_tiles, 1) : 0;
+    cu.n_pos = cu.item < n_items ? max(n_tiles_of(cu.it), 1) : 0;
   };
   auto advance = [&](Cursor& cu) {
     if (++cu.j < cu.n_pos) return;
@@ -193,8 +215,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // row Nq-1 (their results are never stored).
   const uint32_t flip = negate_q ? 0x80008000u : 0u;  // exact sign flip for a negative scale
   auto load_q = [&](const Item& it, u32x4 (&dst)[C::KS]) {
-    const int qi = it.q0 + wave * 32 + col;
-    const u32x4* src = reinterpret_cast<const u32x4*>(Q + it.qbase + (size_t)min(qi, it.Nq - 1) * rs);
+    const int qi = q0_of(it) + wave * 32 + col;
+    const u32x4* src =
+        reinterpret_cast<const u32x4*>(Q + qbase_of(it) + (size_t)min(qi, Nq_of(it) - 1) * rs);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) dst[s] = src[2 * s + half];
   };
@@ -238,10 +261,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // no key tile (an item with no visible key) loads nothing.
   auto load_tile = [&](const Cursor& cu) {
     const Item& it = cu.it;
-    if (it.n_tiles == 0) return;
+    if (n_tiles_of(it) == 0) return;
     const int k0 = cu.j * BC;
-    const char* base = reinterpret_cast<const char*>((k_mover ? K : V) + it.kbase + (size_t)k0 * rs);
-    const int last = it.Nk - 1 - k0;
+    const char* base = reinterpret_cast<const char*>((k_mover ? K : V) + kbase_of(it) + (size_t)k0 * rs);
+    const int last = Nk_of(it) - 1 - k0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = min(first_key + key_step * i, last);
@@ -351,19 +374,32 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   };
   auto softmax = [&](const Item& it, int j) {
     const int k0 = j * BC;
-    const int off = it.Nk - it.Nq;  // bottom-right causal alignment
-    const int wq0 = it.q0 + wave * 32;
-    const bool need_mask = (k0 + BC > it.Nk) || (CAUSAL && k0 + BC - 1 > wq0 + off);
+    const int Nk = Nk_of(it);
+    const int off = Nk - Nq_of(it);  // bottom-right causal alignment
+    const int wq0 = q0_of(it) + wave * 32;
+    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wq0 + off);
     if (__builtin_expect(need_mask, 0)) {
       [[unlikely]];
-      const int lim = CAUSAL ? min(it.Nk - 1, wq0 + col + off) : it.Nk - 1;
+      // Register r of block kb holds key k0 + 32 kb + 4 half + 8 (r/4) + r%4;
+      // it is hidden iff 8 (r/4) + r%4 > room(kb).  Each test and its select
+      // go through VCC as one pair, so the 64 tests never sit in scalar
+      // registers at once.
+      // The compiler does not guard inline assembly against reading a
+      // matrix product too early: 32 wait states first (more than an
+      // 8-pass product needs before a vector read of its result).
+      const int lim = CAUSAL ? min(Nk - 1, wq0 + col + off) : Nk - 1;
+      const float ninf = kNegInf;
+      asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        const int room = lim - k0 - kb * 32 - 4 * half;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > lim) sacc[kb][r] = kNegInf;
-        }
+        for (int r = 0; r < 16; ++r)
+          asm volatile("v_cmp_gt_i32 vcc, %[pos], %[room]\n\tv_cndmask_b32 %[x], %[x], %[ninf], vcc"
+                       : [x] "+v"(sacc[kb][r])
+                       : [pos] "i"(8 * (r >> 2) + (r & 3)), [room] "v"(room), [ninf] "v"(ninf)
+                       : "vcc");
+      }
     }
     // Until a row has a reference (m_ref = -inf: its first tile with a
     // visible key) the wave goes straight to the exact path; otherwise it
@@ -398,11 +434,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // One division per row, O in bf16, LSE = ln2 * (m + log2 l); then the
   // running state starts again for the next item.
   auto epilogue = [&](const Item& it) {
-    const int qi = it.q0 + wave * 32 + col;
+    const int qi = q0_of(it) + wave * 32 + col;
     const float l_tot = sum_across_halves(l_part);
-    if (qi < it.Nq) {
+    if (qi < Nq_of(it)) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      bf16* orow = O + it.qbase + (size_t)qi * rs;
+      bf16* orow = O + qbase_of(it) + (size_t)qi * rs;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -412,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * half) = w;
         }
       if (half == 0)
-        LSE[it.lse_base + qi] = l_tot > 0.f ? (m_ref + log2_hw(l_tot)) * kLn2 : kNegInf;
+        LSE[lse_base_of(it) + qi] = l_tot > 0.f ? (m_ref + log2_hw(l_tot)) * kLn2 : kNegInf;
     }
 #pragma unroll
     for (int i = 0; i < C::NDB; ++i) oacc[i] = f32x16{};
