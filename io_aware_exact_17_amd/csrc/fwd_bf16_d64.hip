@@ -419,13 +419,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
       mx = max_across_halves(mx);
       const float m_new = fmaxf(m_ref, mx * c);  // c > 0, so -inf stays -inf
-      if (m_new != m_ref) {
-        const float alpha = exp2_hw(m_ref - m_new);  // 0 when m_ref was -inf
+      // Rows without a reference have O = 0 and l = 0 (no P was formed
+      // against m = -inf), so a wave where no row had one skips the rescale.
+      if (wave_any(m_ref != kNegInf && m_new != m_ref)) {
+        const float alpha = m_new != m_ref ? exp2_hw(m_ref - m_new) : 1.f;  // 0 from -inf
         l_part *= alpha;
 #pragma unroll
         for (int i = 0; i < C::NDB; ++i) oacc[i] *= alpha;
-        m_ref = m_new;
       }
+      m_ref = m_new;
       exp_tile(m_ref == kNegInf ? 0.f : m_ref, lsum);
     }
     l_part += lsum;
