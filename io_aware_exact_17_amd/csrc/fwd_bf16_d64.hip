@@ -130,8 +130,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   // ------------------------------------------------------------- the items
   // An item is kept as a few integers; row bases, lengths and tile counts
-  // are derived on use (dense: from the kernel arguments), which keeps the
-  // three cursors below within the scalar registers.
+  // are derived on use (dense: from the kernel arguments), so the three
+  // cursors below cost few scalar registers.
   struct Item {
     int qt;      // query tile
     int bh;      // batch-head (dense) or head (varlen)
