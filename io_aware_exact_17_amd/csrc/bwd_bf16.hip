@@ -40,6 +40,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kRows = 32;                  // rows of a fixed block per wave, and of a moving block
 constexpr int kFixed = kWaves * kRows;     // fixed rows per workgroup
+constexpr int kDkdvBufs = 4;               // LDS buffers of the moving Q / dO blocks (dK/dV)
 
 // LDS slot of 16-byte chunk c of tile row r (the forward's permutation):
 // a chunk read across 32 rows and the transposing reads are conflict-free.
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dv,
     float* __restrict__ dK, float* __restrict__ dV, int BH, int Nq, int Nk, float c, float scale) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * (2 * T::BYTES + 2 * kRows * 4)];
+  __shared__ __attribute__((aligned(1024))) char smem[kDkdvBufs * (2 * T::BYTES + 2 * kRows * 4)];
   lds_char* const lds = (lds_char*)smem;
   auto q_tile = [&](int buf) { return lds + buf * (2 * T::BYTES + 256); };
   auto do_tile = [&](int buf) { return q_tile(buf) + T::BYTES; };
@@ -275,18 +276,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     if (tid < 2 * kRows) reinterpret_cast<__attribute__((address_space(3))) float*>(st_tile(buf))[tid] = st;
   };
 
-  // Block qb+1 is fetched into registers during block qb-1 and written to
+  // Four LDS buffers; block j (counted from qb_first) uses buffer j % 4.
+  // Block qb+2 is fetched into registers during block qb-1 and written to
   // LDS in the middle of block qb (between its last LDS reads and its
-  // softmax, when the LDS is otherwise idle); the barrier at the end of
-  // block qb publishes it.
+  // softmax, when the LDS is otherwise idle).  A barrier follows every
+  // second block: block j writes buffer (j+2) % 4, last read by block j-2,
+  // and reads buffer j % 4, written in block j-2; a barrier lies between
+  // the two in both cases (after block j-1 when j is even, after block j-2
+  // when j is odd).
   if (qb_first < n_qb) {
     fetch(qb_first);
     store(0);
-    if (qb_first + 1 < n_qb) fetch(qb_first + 1);
+    if (qb_first + 1 < n_qb) {
+      fetch(qb_first + 1);
+      store(1);
+    }
+    if (qb_first + 2 < n_qb) fetch(qb_first + 2);
     __syncthreads();
   }
   for (int qb = qb_first; qb < n_qb; ++qb) {
-    const int buf = (qb - qb_first) & 1;
+    const int buf = (qb - qb_first) & (kDkdvBufs - 1);
     {
       const lds_char* qt = q_tile(buf);
       const lds_char* dt = do_tile(buf);
@@ -323,11 +332,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         tq[db] = tr_op<D>(qt, lane, db, 0);
       }
       pause_scores(S, dP);
-      if (qb + 1 < n_qb) {
-        // buffer buf ^ 1 was last read in the previous iteration, which
-        // every wave finished before that iteration's barrier
-        store(buf ^ 1);
-        if (qb + 2 < n_qb) fetch(qb + 2);
+      if (qb + 2 < n_qb) {
+        // buffer (buf + 2) % 4 was last read two blocks ago, before a barrier
+        store((buf + 2) & (kDkdvBufs - 1));
+        if (qb + 3 < n_qb) fetch(qb + 3);
       }
       float P[16], dS[16];
       const int key = k0w + col;
@@ -387,7 +395,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         mm_acc(dk[db], uq[db], sb[1]);
       }
     }
-    if (qb + 1 < n_qb) __syncthreads();
+    if (((qb - qb_first) & 1) && qb + 1 < n_qb) __syncthreads();
   }
 
   // dK^T / dV^T accumulators: lane = key, register r of dim block db =
