@@ -41,6 +41,7 @@ constexpr int kWaves = 4;
 constexpr int kRows = 32;                  // rows of a fixed block per wave, and of a moving block
 constexpr int kFixed = kWaves * kRows;     // fixed rows per workgroup
 constexpr int kDkdvBufs = 4;               // LDS buffers of the moving Q / dO blocks (dK/dV)
+constexpr int kDqBufs = 4;                 // LDS buffers of the moving K / V blocks (dQ)
 
 // LDS slot of 16-byte chunk c of tile row r (the forward's permutation):
 // a chunk read across 32 rows and the transposing reads are conflict-free.
@@ -423,14 +424,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 // -------------------------------------------------------------------- dQ
 // Workgroup: 4 waves x 32 queries; query tile qt = n_qt - 1 - blockIdx.x / BH
 // (late queries, which see the most keys, first).  The key blocks stream
-// through LDS (K, V), double-buffered.
+// through four LDS buffers (K, V), two blocks per barrier.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dv,
     float* __restrict__ dQ, int BH, int Nq, int Nk, float c, float scale, int n_qt) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * T::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[kDqBufs * 2 * T::BYTES];
   lds_char* const lds = (lds_char*)smem;
   auto k_tile = [&](int buf) { return lds + buf * 2 * T::BYTES; };
   auto v_tile = [&](int buf) { return k_tile(buf) + T::BYTES; };
@@ -483,16 +484,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       copy_to_lds(vg, off, dst + T::BYTES + i * 1024);
     }
   };
+  // Four LDS buffers; key block kb uses buffer kb % 4.  Block kb + 2 is
+  // copied at the start of block kb, and every second block ends with a
+  // wait for all copies and a barrier: block kb writes buffer (kb+2) % 4,
+  // last read by block kb-2, and reads buffer kb % 4, whose copies were
+  // waited for before the barrier after block kb-1 (kb even) or kb-2 (kb
+  // odd); a barrier lies between each pair.
   if (n_kb > 0) {
     stage(0, 0);
+    if (n_kb > 1) stage(1, 1);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
   }
   for (int kb = 0; kb < n_kb; ++kb) {
-    const int buf = kb & 1;
-    // buffer buf ^ 1 was last read in the previous iteration, which every
-    // wave finished before that iteration's barrier
-    if (kb + 1 < n_kb) stage(kb + 1, buf ^ 1);
+    const int buf = kb & (kDqBufs - 1);
+    if (kb + 2 < n_kb) stage(kb + 2, (kb + 2) & (kDqBufs - 1));
     {  // blocks past this wave's last visible key are masked whole
       const lds_char* kt_ = k_tile(buf);
       const lds_char* vt = v_tile(buf);
@@ -570,7 +576,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int db = 0; db < T::NDB; ++db) mm_acc(acc[db], uk[db], sb[1]);
     }
-    if (kb + 1 < n_kb) {
+    if ((kb & 1) && kb + 1 < n_kb) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
     }
