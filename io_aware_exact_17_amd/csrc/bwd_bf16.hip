@@ -40,7 +40,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kRows = 32;                  // rows of a fixed block per wave, and of a moving block
 constexpr int kFixed = kWaves * kRows;     // fixed rows per workgroup
-constexpr int kDkdvBufs = 4;               // LDS buffers of the moving Q / dO blocks (dK/dV)
+constexpr int kDkdvBufs = 8;               // LDS buffers of the moving Q / dO blocks (dK/dV)
+constexpr int kDkdvAhead = kDkdvBufs / 2;  // blocks staged ahead; blocks per barrier
 constexpr int kDqBufs = 4;                 // LDS buffers of the moving K / V blocks (dQ)
 
 // LDS slot of 16-byte chunk c of tile row r (the forward's permutation):
@@ -277,22 +278,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     if (tid < 2 * kRows) reinterpret_cast<__attribute__((address_space(3))) float*>(st_tile(buf))[tid] = st;
   };
 
-  // Four LDS buffers; block j (counted from qb_first) uses buffer j % 4.
-  // Block qb+2 is fetched into registers during block qb-1 and written to
-  // LDS in the middle of block qb (between its last LDS reads and its
-  // softmax, when the LDS is otherwise idle).  A barrier follows every
-  // second block: block j writes buffer (j+2) % 4, last read by block j-2,
-  // and reads buffer j % 4, written in block j-2; a barrier lies between
-  // the two in both cases (after block j-1 when j is even, after block j-2
-  // when j is odd).
+  // kDkdvBufs LDS buffers; block j (counted from qb_first) uses buffer
+  // j % kDkdvBufs.  With A = kDkdvAhead = kDkdvBufs / 2, block qb+A is
+  // fetched into registers during block qb-1 and written to LDS in the
+  // middle of block qb (between its last LDS reads and its softmax, when the
+  // LDS is otherwise idle).  A barrier follows every A-th block (j % A =
+  // A-1): block j writes buffer (j+A) % kDkdvBufs, last read by block j-A,
+  // and reads buffer j % kDkdvBufs, written in block j-A; of the A blocks
+  // j-A .. j-1 exactly one ends with a barrier, which lies after block j-A's
+  // accesses and before block j's.
   if (qb_first < n_qb) {
-    fetch(qb_first);
-    store(0);
-    if (qb_first + 1 < n_qb) {
-      fetch(qb_first + 1);
-      store(1);
+    for (int i = 0; i < kDkdvAhead && qb_first + i < n_qb; ++i) {
+      fetch(qb_first + i);
+      store(i);
     }
-    if (qb_first + 2 < n_qb) fetch(qb_first + 2);
+    if (qb_first + kDkdvAhead < n_qb) fetch(qb_first + kDkdvAhead);
     __syncthreads();
   }
   for (int qb = qb_first; qb < n_qb; ++qb) {
@@ -333,10 +333,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         tq[db] = tr_op<D>(qt, lane, db, 0);
       }
       pause_scores(S, dP);
-      if (qb + 2 < n_qb) {
-        // buffer (buf + 2) % 4 was last read two blocks ago, before a barrier
-        store((buf + 2) & (kDkdvBufs - 1));
-        if (qb + 3 < n_qb) fetch(qb + 3);
+      if (qb + kDkdvAhead < n_qb) {
+        // buffer (buf + A) % kDkdvBufs was last read A blocks ago, before a barrier
+        store((buf + kDkdvAhead) & (kDkdvBufs - 1));
+        if (qb + kDkdvAhead + 1 < n_qb) fetch(qb + kDkdvAhead + 1);
       }
       float P[16], dS[16];
       const int key = k0w + col;
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         mm_acc(dk[db], uq[db], sb[1]);
       }
     }
-    if (((qb - qb_first) & 1) && qb + 1 < n_qb) __syncthreads();
+    if ((qb - qb_first) % kDkdvAhead == kDkdvAhead - 1 && qb + 1 < n_qb) __syncthreads();
   }
 
   // dK^T / dV^T accumulators: lane = key, register r of dim block db =
