@@ -85,6 +85,14 @@ def _check(status: int, where: str):
         raise FAError(status, where)
 
 
+def _on_device(t):
+    """Make t's device current for the call: kernels launched on the default
+    (null) stream go to the current device."""
+    import torch
+
+    return torch.cuda.device(t.device)
+
+
 def _stream(t, stream):
     import torch
 
@@ -129,8 +137,9 @@ def _fwd(entry, dtype, q, k, v, scale, causal, out, lse, stream):
     pl = _dev(lse, "lse", torch.float32, 3)
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, Nq):
         raise ValueError("out / lse shape mismatch")
-    st = getattr(lib, entry)(pq, pk, pv, po, pl, B, H, Nq, Nk, d, float(scale), int(bool(causal)),
-                             _stream(q, stream))
+    with _on_device(q):
+        st = getattr(lib, entry)(pq, pk, pv, po, pl, B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+                                 _stream(q, stream))
     _check(st, entry)
     return out, lse
 
@@ -179,8 +188,9 @@ def fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False, out=None,
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     po = _dev(out, "out", torch.bfloat16, 4)
     pl = _dev(lse, "lse", torch.float32, 3)
-    st = lib.fa_fwd_block_sparse(pq, pk, pv, po, pl, pm, B, H, Nq, Nk, d, float(scale),
-                                 1 if causal else 0, _stream(q, stream))
+    with _on_device(q):
+        st = lib.fa_fwd_block_sparse(pq, pk, pv, po, pl, pm, B, H, Nq, Nk, d, float(scale),
+                                     1 if causal else 0, _stream(q, stream))
     _check(st, "fa_fwd_block_sparse")
     return out, lse
 
@@ -215,8 +225,9 @@ def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv
         workspace = torch.empty(max(fa_bwd_workspace_bytes(B, H, Nq), 16), dtype=torch.uint8,
                                 device=q.device)
     pw = _dev(workspace, "workspace", torch.uint8, 1)
-    st = lib.fa_bwd(*ptrs, pl, *gp, B, H, Nq, Nk, d, float(scale), 1 if causal else 0, pw,
-                    workspace.numel(), _stream(q, stream))
+    with _on_device(q):
+        st = lib.fa_bwd(*ptrs, pl, *gp, B, H, Nq, Nk, d, float(scale), 1 if causal else 0, pw,
+                        workspace.numel(), _stream(q, stream))
     _check(st, "fa_bwd")
     return dq, dk, dv
 
@@ -248,8 +259,9 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None,
         lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
     po = _dev(out, "out", torch.bfloat16, 3)
     pl = _dev(lse, "lse", torch.float32, 2)
-    st = lib.fa_fwd_varlen(pq, pk, pv, po, pl, pcq, pck, B, H, d, Tq, int(max_seqlen_q),
-                           float(scale), 1 if causal else 0, _stream(q, stream))
+    with _on_device(q):
+        st = lib.fa_fwd_varlen(pq, pk, pv, po, pl, pcq, pck, B, H, d, Tq, int(max_seqlen_q),
+                               float(scale), 1 if causal else 0, _stream(q, stream))
     _check(st, "fa_fwd_varlen")
     return out, lse
 
@@ -289,8 +301,9 @@ def fa_decode_varlen(q, kcache, vcache, seqlens, offsets, max_seqlen, scale=None
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     pw = _dev(workspace, "workspace", torch.uint8, 1)
-    st = lib.fa_decode_varlen(pq, pk, pv, ps, po_, po, pl, B, H, d, int(max_seqlen), float(scale),
-                              int(split_keys), pw, workspace.numel(), _stream(q, stream))
+    with _on_device(q):
+        st = lib.fa_decode_varlen(pq, pk, pv, ps, po_, po, pl, B, H, d, int(max_seqlen), float(scale),
+                                  int(split_keys), pw, workspace.numel(), _stream(q, stream))
     _check(st, "fa_decode_varlen")
     return out, lse
 
@@ -332,9 +345,10 @@ def fa_decode_paged(q, kpages, vpages, block_table, seqlens, max_seqlen, scale=N
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     pw = _dev(workspace, "workspace", torch.uint8, 1)
-    st = lib.fa_decode_paged(pq, pk, pv, pb, ps, po, pl, B, H, d, int(page_size), int(num_pages),
-                             int(block_table.shape[1]), int(max_seqlen), float(scale),
-                             int(split_keys), pw, workspace.numel(), _stream(q, stream))
+    with _on_device(q):
+        st = lib.fa_decode_paged(pq, pk, pv, pb, ps, po, pl, B, H, d, int(page_size), int(num_pages),
+                                 int(block_table.shape[1]), int(max_seqlen), float(scale),
+                                 int(split_keys), pw, workspace.numel(), _stream(q, stream))
     _check(st, "fa_decode_paged")
     return out, lse
 
@@ -352,6 +366,7 @@ def fa_probe_read(buf, nbytes=None, sink=None, stream=None):
         raise ValueError("nbytes exceeds the buffer")
     if sink is None:
         sink = torch.empty(1, dtype=torch.int32, device=buf.device)
-    st = load().fa_probe_read(ctypes.c_void_p(buf.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
-                              _stream(buf, stream))
+    with _on_device(buf):
+        st = load().fa_probe_read(ctypes.c_void_p(buf.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+                                  _stream(buf, stream))
     _check(st, "fa_probe_read")
