@@ -297,6 +297,7 @@ D64_STREAM = [
     (1, 128, 600, 100, True),
     (2, 100, 300, 333, False),
     (1, 96, 1000, 1000, True),
+    (5, 67, 600, 600, True),   # B*H = 335, odd: 1005 query tiles, no head-to-XCD alignment
 ]
 
 
