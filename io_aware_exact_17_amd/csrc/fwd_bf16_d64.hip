@@ -59,38 +59,42 @@ namespace fa {
 
 namespace {
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
 constexpr int kThreads = 512;
-constexpr int kMovers = 256;      // threads staging each operand
 constexpr int kBR = 256;          // query rows per workgroup (8 waves x 32)
-constexpr int kKBuf = 2;          // LDS K buffers
-constexpr int kVBuf = 3;          // LDS V^T buffers
+constexpr int kKBuf = 4;          // LDS K buffers
+constexpr int kVBuf = 5;          // LDS V buffers (group B reads the previous position's V)
 constexpr float kSumBound = 256.f;  // a tile's P sum per lane half stays <= 2^8
 constexpr int kPrefetch = 6;      // LDS operand reads kept ahead of the matrix cores
 constexpr int kMaxDevices = 64;   // devices whose CU count is cached
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BC = 8192 / D;    // keys per tile: 64 for d=128, 128 for d=64
+  static constexpr int BC = 8192 / D;    // keys per tile: 128 for d=64
   static constexpr int KS = D / 16;      // k-steps of S^T = K Q^T
   static constexpr int NKB = BC / 32;    // 32-key blocks per tile
   static constexpr int NDB = D / 32;     // 32-row blocks of O^T
-  static constexpr int KROW = D + 8;     // LDS row stride of K (elements)
-  static constexpr int VROW = BC + 8;    // LDS row stride of V^T (elements)
-  static constexpr int KTILE = BC * KROW;
-  static constexpr int VTILE = D * VROW;
-  static constexpr int KCHUNKS = BC * D / 8 / kMovers;   // 16-byte K chunks per K mover
-  static constexpr int VBLOCKS = (BC / 4) * (D / 8);     // 4-key x 8-dim V blocks per tile
-  static constexpr int LDS_ELEMS = kKBuf * KTILE + kVBuf * VTILE;
-  static_assert(KCHUNKS == 4 && KCHUNKS * kMovers * 8 == BC * D, "K tile split");
-  static_assert(VBLOCKS == kMovers, "one V block per V mover");
+  static constexpr int ROWB = D * 2;     // bytes per tile row
+  static constexpr int CPR = D / 8;      // 16-byte chunks per row
+  static constexpr int TILE = BC * ROWB;            // bytes per K or V tile
+  static constexpr int RPI = 1024 / ROWB;           // tile rows per 1 KB wave instruction
+  static constexpr int IPW = TILE / 1024 / (kThreads / 64);  // wave instructions per tile per wave
+  static constexpr int LDS_BYTES = (kKBuf + kVBuf) * TILE;
+  static_assert(D == 64, "the LDS layout below is written for d = 64");
+  static_assert(IPW * 1024 * (kThreads / 64) == TILE, "tile copies split evenly over the waves");
 };
 
-// Position of a group of four keys inside its group of 16 in the V^T layout:
-// the two middle groups are swapped, so positions 8h..8h+7 hold keys
-// {4h..4h+3, 8+4h..8+4h+3} — the keys accumulator registers 0..7 of lane
-// half h cover in the S^T layout.
-__device__ __forceinline__ int vt_pos4(int group4) {
-  return ((group4 & 1) << 1) | ((group4 >> 1) & 1);
+// LDS slot of 16-byte chunk c of tile row r (rows of 128 bytes, two per
+// 256-byte bank line): c ^ f(r) with f(r) = (bit 1 of r) << 2 | bits 2-3 of
+// r.  A K operand read (one chunk of 16 consecutive rows per 16 lanes) and a
+// transposing V read (4 rows x 4 chunks) then touch 16 distinct 16-byte bank
+// groups.  The permutation is its own inverse.
+__device__ __forceinline__ int swz64(int r, int c) {
+  return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // The work is a list of items, one per (sequence or batch-head, query tile),
@@ -115,9 +119,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int32_t* __restrict__ cu_k, int H, int total_q) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
-  __shared__ __attribute__((aligned(16))) bf16 smem[C::LDS_ELEMS];
-  bf16* const sK = smem;                      // kKBuf K tiles
-  bf16* const sV = smem + kKBuf * C::KTILE;   // kVBuf V^T tiles
+  constexpr int ROWB = C::ROWB;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  lds_char* const lds = (lds_char*)smem;  // kKBuf K tiles, then kVBuf V tiles
+  constexpr int VREG = kKBuf * C::TILE;   // byte offset of the V tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,59 +244,63 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   };
 
   // ---------------------------------------------------------- tile staging
-  // Waves 0-3 move V, waves 4-7 move K, four 16-byte chunks per thread.
-  //   K mover mt: chunks mt + 256 i of the row-major tile, i.e. key
-  //     mt / (D/8) + (256 / (D/8)) i, 8 dims at (mt % (D/8)) * 8.
-  //   V mover mt: keys 4*vkg .. 4*vkg+3 of dims vdb*8 .. vdb*8+7, written to
-  //     V^T transposed.
-  // Position p of the stream uses K buffer p % kKBuf and V^T buffer p % kVBuf.
-  const bool k_mover = tid >= kMovers;
-  const int mt = tid & (kMovers - 1);
-  constexpr int kKeysPerPass = kMovers / (D / 8);
-  const int vkg = mt % (BC / 4);
-  const int vdb = mt / (BC / 4);
-  const int first_key = k_mover ? mt / (D / 8) : 4 * vkg;
-  const int key_step = k_mover ? kKeysPerPass : 1;
-  const int dcol = k_mover ? (mt % (D / 8)) * 8 : vdb * 8;
-  u32x4 stg[4];
-
-  // The tile base is uniform, so loads take an SGPR base plus a 32-bit lane
-  // byte offset.  Keys past Nk read row Nk-1 instead: finite values whose
-  // scores are masked to -inf, so they carry zero weight.  A position with
-  // no key tile (an item with no visible key) loads nothing.
-  auto load_tile = [&](const Cursor& cu) {
+  // K and V tiles (BC keys x 128 bytes, row-major, 16-byte chunks permuted
+  // by swz64) go from memory straight into LDS with global_load_lds_dwordx4:
+  // wave instruction ii fills tile rows ii*RPI .. ii*RPI+RPI-1 (1 KB, lane
+  // l at byte 16 l, i.e. row l / CPR, slot l % CPR), so the lane fetches the
+  // chunk that slot holds.  Each of the 8 waves issues IPW instructions per
+  // operand.  Keys past Nk fetch row Nk-1 (finite values whose scores are
+  // masked to -inf).  Stream position p uses K buffer p % kKBuf and V buffer
+  // p % kVBuf; a position with no key tile (an item with no visible key)
+  // copies nothing.
+  const int ld_row = lane / C::CPR;
+  const int ld_slot = lane % C::CPR;
+  const uint32_t rsb = (uint32_t)rs * 2;  // bytes between consecutive rows of a head
+  const uint32_t lds_wave =
+      (uint32_t)(size_t)lds + __builtin_amdgcn_readfirstlane(wave) * C::IPW * 1024;  // uniform
+  auto issue_tile = [&](const Cursor& cu, int p) {
     const Item& it = cu.it;
     if (n_tiles_of(it) == 0) return;
     const int k0 = cu.j * BC;
-    const char* base = reinterpret_cast<const char*>((k_mover ? K : V) + kbase_of(it) + (size_t)k0 * rs);
     const int last = Nk_of(it) - 1 - k0;
+    const char* kg = reinterpret_cast<const char*>(K + kbase_of(it) + (size_t)k0 * rs);
+    const char* vg = reinterpret_cast<const char*>(V + kbase_of(it) + (size_t)k0 * rs);
+    uint32_t kdst = lds_wave + (p % kKBuf) * C::TILE;
+    uint32_t vdst = lds_wave + VREG + (p % kVBuf) * C::TILE;
+    asm volatile("" : "+s"(kdst), "+s"(vdst));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(first_key + key_step * i, last);
-      stg[i] = *reinterpret_cast<const u32x4*>(base + (uint32_t)((key * rs + dcol) * 2));
+    for (int i = 0; i < C::IPW; ++i) {
+      const int r = (wave * C::IPW + i) * C::RPI + ld_row;
+      const uint32_t off = (uint32_t)min(r, last) * rsb + (uint32_t)(swz64(r, ld_slot) * 16);
+      copy_to_lds(kg, off, kdst + i * 1024);
+      copy_to_lds(vg, off, vdst + i * 1024);
     }
   };
-  auto store_tile = [&](int p) {
-    if (k_mover) {
-      bf16* sk = sK + (p % kKBuf) * C::KTILE;
+
+  // LDS read offsets.  K operand of k-step s: key row col (+32 per key
+  // block), chunk 2s + half.  V^T operand of dim block db for a 16-key group
+  // (two transposing reads cc = 0, 1): lane l addresses key 8cc + 4 half +
+  // (l%16)/4 of the group and dims d..d+3, d = 32 db + 16 ((l/16)%2) +
+  // 4 (l%4); ds_read_b64_tr_b16 then hands each lane, for its own dim, the
+  // four keys its P registers hold (keys 4h..4h+3 and 8+4h..8+4h+3 of the
+  // group for lane half h).  The permutation depends on the row modulo 16,
+  // so key blocks and groups are immediate offsets.
+  uint32_t k_off[C::KS];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(sk + (first_key + key_step * i) * C::KROW + dcol) = stg[i];
-    } else {
-      bf16* sv = sV + (p % kVBuf) * C::VTILE;
-      // 4 keys x 8 dims -> 8 rows of V^T, 4 keys each.
-      const int pos = 16 * (vkg >> 2) + 4 * vt_pos4(vkg & 3);
+  for (int st = 0; st < C::KS; ++st) k_off[st] = (uint32_t)(col * ROWB + swz64(col, 2 * st + half) * 16);
+  uint32_t v_off[2][C::NDB];
+  {
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t e01 = __builtin_amdgcn_perm(stg[1][i], stg[0][i], 0x05040100u);
-        const uint32_t e23 = __builtin_amdgcn_perm(stg[3][i], stg[2][i], 0x05040100u);
-        const uint32_t o01 = __builtin_amdgcn_perm(stg[1][i], stg[0][i], 0x07060302u);
-        const uint32_t o23 = __builtin_amdgcn_perm(stg[3][i], stg[2][i], 0x07060302u);
-        *reinterpret_cast<u32x2*>(sv + (vdb * 8 + 2 * i) * C::VROW + pos) = u32x2{e01, e23};
-        *reinterpret_cast<u32x2*>(sv + (vdb * 8 + 2 * i + 1) * C::VROW + pos) = u32x2{o01, o23};
+    for (int cc = 0; cc < 2; ++cc) {
+      const int key = 8 * cc + 4 * half + ((lane & 15) >> 2);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const int d = 32 * db + tr_dim;
+        v_off[cc][db] = (uint32_t)(VREG + key * ROWB + swz64(key, d >> 3) * 16 + (d & 7) * 2);
       }
     }
-  };
+  }
 
   // ------------------------------------------------------ per-tile stages
   f32x16 oacc[C::NDB];
@@ -302,17 +311,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   f32x16 sacc[C::NKB];
   uint32_t pk[C::NKB][8];  // bf16 P pairs of the latest softmax
 
-  // Matrix-core loops keep kPrefetch LDS operand reads in flight: the
-  // schedule is pinned to  kPrefetch reads, then (1 MFMA, 1 read) pairs,
-  // then the remaining MFMAs, so no MFMA waits on a read issued just before.
-  auto pipeline_schedule = [&](auto n_mfma) {
+  // Matrix-core loops keep the LDS operands of kPrefetch products in
+  // flight (R reads per product): the schedule is pinned to kPrefetch * R
+  // reads, then (1 MFMA, R reads) groups, then the remaining MFMAs, so no
+  // MFMA waits on a read issued just before.
+  auto pipeline_schedule = [&](auto n_mfma, auto reads_per_mfma) {
     constexpr int N = decltype(n_mfma)::value;
+    constexpr int R = decltype(reads_per_mfma)::value;
 #pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < kPrefetch * R; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + kPrefetch < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i + kPrefetch < N) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
     }
   };
 
@@ -320,36 +331,41 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // neighbouring wave's vector work fills the gaps instead of delaying it.
   auto qk = [&](int p) {
     __builtin_amdgcn_s_setprio(1);
-    const bf16* sk = sK + (p % kKBuf) * C::KTILE + col * C::KROW + half * 8;
+    const lds_char* sk = lds + (p % kKBuf) * C::TILE;
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s)
+    for (int st = 0; st < C::KS; ++st)
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + kb * 32 * C::KROW + s * 16);
-        sacc[kb] = mfma_32x32x16(a, qf[s], sacc[kb]);
+        const bf16x8 a = *reinterpret_cast<const lds_bf16x8*>(sk + kb * 32 * ROWB + k_off[st]);
+        sacc[kb] = mfma_32x32x16(a, qf[st], sacc[kb]);
       }
-    pipeline_schedule(std::integral_constant<int, C::KS * C::NKB>{});
+    pipeline_schedule(std::integral_constant<int, C::KS * C::NKB>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_s_setprio(0);
   };
 
   auto pv = [&](int p) {
     __builtin_amdgcn_s_setprio(1);
-    const bf16* sv = sV + (p % kVBuf) * C::VTILE + col * C::VROW + half * 8;
+    const lds_char* sv = lds + (p % kVBuf) * C::TILE;  // v_off carries the V region offset
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bf16x8 b = __builtin_bit_cast(
             bf16x8, u32x4{pk[kb][4 * t], pk[kb][4 * t + 1], pk[kb][4 * t + 2], pk[kb][4 * t + 3]});
+        const lds_char* grp = sv + (2 * kb + t) * 16 * ROWB;  // 16-key group 2kb + t
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sv + db * 32 * C::VROW + (2 * kb + t) * 16);
+          const u32x2 lo = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(grp + v_off[0][db])));
+          const u32x2 hi = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(grp + v_off[1][db])));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
           oacc[db] = mfma_32x32x16(a, b, oacc[db]);
         }
       }
-    pipeline_schedule(std::integral_constant<int, C::NKB * 2 * C::NDB>{});
+    pipeline_schedule(std::integral_constant<int, C::NKB * 2 * C::NDB>{}, std::integral_constant<int, 2>{});
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -459,13 +475,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   };
 
   // ------------------------------------------------------------- main loop
-  // Position 0 is staged and position 1 fetched before the first barrier;
-  // `ld` is the position whose tile the staging registers hold or will hold.
+  // The copies of position p+2 are issued at the start of position p, and
+  // every second position (p odd) ends with a wait for all copies and a
+  // barrier.  Position p's copies go to K buffer (p+2) % 4, last read at
+  // position p-2, and V buffer (p+2) % 5, last read at p-2 by group B; a
+  // barrier lies between (after p-1 when p is even, after p-2 when it is
+  // odd).  Position p reads what was copied at p-2 and waited for at that
+  // same barrier.  Positions 0 and 1 are copied before the first barrier;
+  // `ld` is the next position to copy.
   Cursor ld = cur;
-  load_tile(ld);
-  store_tile(0);
+  issue_tile(ld, 0);
   advance(ld);
-  if (ld.item < n_items) load_tile(ld);
+  if (ld.item < n_items) {
+    issue_tile(ld, 1);
+    advance(ld);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
   // Group B finishes the previous position's P V first, so the stream ends
@@ -475,6 +500,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   for (int p = 0; cur.item < n_items || prv.item < n_items; ++p) {
     const bool have_cur = cur.item < n_items;
     const Item& ic = cur.it;
+    if (ld.item < n_items) {
+      issue_tile(ld, p + 2);
+      advance(ld);
+    }
     if (!group_b) {
       if (have_cur) {
         prefetch_q(cur);
@@ -505,13 +534,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         }
       }
     }
-    // Stage position p+1 (fetched one step ago) and fetch position p+2.
-    if (ld.item < n_items) {
-      store_tile(p + 1);
-      advance(ld);
-      if (ld.item < n_items) load_tile(ld);
+    if (p & 1) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();
     }
-    __syncthreads();
     prv = cur;
     if (have_cur) advance(cur);
   }
