@@ -29,14 +29,15 @@
 //    S = K Q^T -> softmax.  After each barrier the two waves sharing a SIMD
 //    therefore run their vector-ALU softmax while the other one feeds the
 //    matrix core, instead of both waiting on the same unit.
-//  * K tiles are staged row-major in LDS; V tiles transposed (V^T, keys
-//    contiguous) with the key order permuted inside each group of 16 so that
-//    one 16-byte LDS read yields exactly the 8 keys a lane's P registers hold.
-//    Row strides are padded by 16 bytes (no bank conflicts).  Two K buffers
-//    and three V^T buffers (group B reads the previous V tile); one barrier
-//    per tile.  The tile after the next is fetched from HBM into registers
-//    with 16-byte loads a whole tile ahead: waves 0-3 move V tiles
-//    (transposing them in registers), waves 4-7 move K tiles.
+//  * K and V tiles (128 keys) go from HBM straight into LDS
+//    (global_load_lds_dwordx4, 1 KB per wave instruction, no staging
+//    registers), both row-major with each row's 16-byte chunks permuted by a
+//    function of the row index, so K operand reads and transposing V reads
+//    are free of bank conflicts.  The V^T operand comes from the row-major V
+//    tile through ds_read_b64_tr_b16, addressed so that each lane receives,
+//    for its own output dim, the keys its P registers hold.  Four K and five
+//    V buffers (group B reads the previous position's V): tiles are copied
+//    two positions ahead and a barrier follows every second position.
 //  * exp is 2^x on v_exp_f32 with log2(e) folded into the scale.  The
 //    reference maximum is not recomputed per tile: P is formed against the
 //    current reference and only when a tile's P sum exceeds 2^8 (so some P
