@@ -348,20 +348,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   auto pv = [&](int p) {
     __builtin_amdgcn_s_setprio(1);
-    const lds_char* sv = lds + (p % kVBuf) * C::TILE;  // v_off carries the V region offset
+    // This lane's read addresses in the buffer, formed once per call and
+    // hidden from re-association, so the 16-key group offsets below fold
+    // into the reads' immediate offsets instead of costing an add per read.
+    uint32_t vb[2][C::NDB];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        vb[cc][db] = (uint32_t)(size_t)lds + (p % kVBuf) * C::TILE + v_off[cc][db];
+        asm volatile("" : "+v"(vb[cc][db]));
+      }
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bf16x8 b = __builtin_bit_cast(
             bf16x8, u32x4{pk[kb][4 * t], pk[kb][4 * t + 1], pk[kb][4 * t + 2], pk[kb][4 * t + 3]});
-        const lds_char* grp = sv + (2 * kb + t) * 16 * ROWB;  // 16-key group 2kb + t
+        constexpr int kGrpBytes = 16 * ROWB;  // one 16-key group
+        const int g = 2 * kb + t;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
           const u32x2 lo = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(grp + v_off[0][db])));
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)(vb[0][db] + g * kGrpBytes)));
           const u32x2 hi = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(grp + v_off[1][db])));
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)(vb[1][db] + g * kGrpBytes)));
           const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
           oacc[db] = mfma_32x32x16(a, b, oacc[db]);
         }
