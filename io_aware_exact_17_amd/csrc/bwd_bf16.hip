@@ -65,29 +65,53 @@ struct Tile {
   static constexpr int NDB = D / 32;           // 32-wide blocks of d
 };
 
-// Row-major operand of one k-step: lane holds row (lane%32), dims
-// 16 s + 8 (lane/32) .. +7.
+// LDS operands of the products.  Row-major operand of one k-step: lane holds
+// row (lane%32), dims 16 s + 8 (lane/32) .. +7.  Transposed operand of dim
+// block db over 16 rows: lane holds dim 32 db + lane%32 of the rows
+// {4h .. 4h+3, 8+4h .. 8+4h+3} (h = lane/32) -- the rows accumulator
+// registers 8t .. 8t+7 of a 32-row block hold -- read with the transposing
+// ds_read_b64_tr_b16.  Both are read through per-lane addresses formed once
+// per block: lane_addr() adds a lane's offset within a tile to the tile's
+// base and hides the sum from re-association, so that constant
+// displacements added afterwards (the dO tile after the Q tile, the second
+// 16 rows of a block) fold into the reads' immediate offsets instead of
+// costing an add per read.
 template <int D>
-__device__ __forceinline__ bf16x8 row_op(const lds_char* tile, int lane, int s) {
+struct OpOffsets {
+  uint32_t row[Tile<D>::KS];     // row operand of k-step s
+  uint32_t tr[Tile<D>::NDB][2];  // transposed operand of dim block db, read cc, rows 0..15
+};
+template <int D>
+__device__ __forceinline__ OpOffsets<D> op_offsets(int lane) {
+  OpOffsets<D> o;
   const int r = lane & 31, h = lane >> 5;
-  return *reinterpret_cast<const lds_bf16x8*>(tile + r * Tile<D>::ROWB + swz<D>(r, 2 * s + h) * 16);
-}
-
-// Transposed operand of dim block db and k-step t (tile rows 16t .. 16t+15):
-// lane holds dim 32 db + lane%32 of the rows 16t + {4h .. 4h+3, 8+4h .. 8+4h+3},
-// h = lane/32 -- the rows accumulator registers 8t .. 8t+7 of a 32-row block hold.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_op(const lds_char* tile, int lane, int db, int t) {
-  const int h = lane >> 5;
-  const int dim = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  u32x2 part[2];
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc) {
-    const int row = 16 * t + 8 * cc + 4 * h + ((lane & 15) >> 2);
-    const lds_char* p = tile + row * Tile<D>::ROWB + swz<D>(row, dim >> 3) * 16 + (dim & 7) * 2;
-    part[cc] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+  for (int s = 0; s < Tile<D>::KS; ++s) o.row[s] = (uint32_t)(r * Tile<D>::ROWB + swz<D>(r, 2 * s + h) * 16);
+#pragma unroll
+  for (int db = 0; db < Tile<D>::NDB; ++db) {
+    const int dim = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int row = 8 * cc + 4 * h + ((lane & 15) >> 2);
+      o.tr[db][cc] = (uint32_t)(row * Tile<D>::ROWB + swz<D>(row, dim >> 3) * 16 + (dim & 7) * 2);
+    }
   }
-  return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
+  return o;
+}
+__device__ __forceinline__ uint32_t lane_addr(const lds_char* tile, uint32_t off) {
+  uint32_t a = (uint32_t)(size_t)tile + off;
+  asm volatile("" : "+v"(a));
+  return a;
+}
+__device__ __forceinline__ bf16x8 row_at(uint32_t a, int disp) {
+  return *reinterpret_cast<const lds_bf16x8*>((size_t)(a + disp));
+}
+// Transposed operand from the two read addresses of a dim block; disp
+// selects the tile (Q or dO, K or V) and the 16-row half (+16 rows).
+__device__ __forceinline__ bf16x8 tr_at(const uint32_t (&a)[2], int disp) {
+  const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)(a[0] + disp)));
+  const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)(a[1] + disp)));
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 // Matrix products written as single instructions so that the score products
@@ -148,6 +172,11 @@ __device__ __forceinline__ void pause_operands(bf16x8 (&a)[2], bf16x8 (&b)[2]) {
 // moved ahead of those products (which would hold their registers longer).
 __device__ __forceinline__ void after_products(const lds_char*& a, const lds_char*& b) {
   asm volatile("" : "+s"(a), "+s"(b));
+}
+template <int N>
+__device__ __forceinline__ void after_products(uint32_t (&a)[N][2]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(a[i][0]), "+v"(a[i][1]));
 }
 
 // Accumulator registers 8t .. 8t+7 packed to bf16 as a B operand.
@@ -264,6 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   Stager<D> sq, sd;
   float st = 0.f;  // this thread's lse2 or D value of the next block (threads 0..63)
+  const OpOffsets<D> oo = op_offsets<D>(lane);
   auto fetch = [&](int qb) {
     sq.fetch(Qh, qb * kRows, Nq, tid);
     sd.fetch(dOh, qb * kRows, Nq, tid);
@@ -314,8 +344,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       bf16x8 qa[T::KS], da[T::KS];
 #pragma unroll
       for (int s = 0; s < T::KS; ++s) {
-        qa[s] = row_op<D>(qt, lane, s);
-        da[s] = row_op<D>(dt, lane, s);
+        const uint32_t a = lane_addr(qt, oo.row[s]);
+        qa[s] = row_at(a, 0);
+        da[s] = row_at(a, T::BYTES);  // the dO tile follows the Q tile
       }
       f32x16 S, dP;
       mm_first(S, qa[0], kf[0]);
@@ -326,11 +357,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         mm_next(dP, da[s], vf[s]);
       }
       // transposed operands of the first 16 queries, read during the wait
+      uint32_t ta[T::NDB][2];
       bf16x8 tdo[T::NDB], tq[T::NDB];
 #pragma unroll
       for (int db = 0; db < T::NDB; ++db) {
-        tdo[db] = tr_op<D>(dt, lane, db, 0);
-        tq[db] = tr_op<D>(qt, lane, db, 0);
+        ta[db][0] = lane_addr(qt, oo.tr[db][0]);
+        ta[db][1] = lane_addr(qt, oo.tr[db][1]);
+        tdo[db] = tr_at(ta[db], T::BYTES);
+        tq[db] = tr_at(ta[db], 0);
       }
       pause_scores(S, dP);
       if (qb + kDkdvAhead < n_qb) {
@@ -376,14 +410,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         mm_acc(dv[db], tdo[db], pb[0]);
         mm_acc(dk[db], tq[db], sb[0]);
       }
-      const lds_char* qt1 = qt;
-      const lds_char* dt1 = dt;
-      after_products(qt1, dt1);
+      after_products(ta);
       bf16x8 udo[T::NDB], uq[T::NDB];
 #pragma unroll
       for (int db = 0; db < T::NDB; ++db) {
-        udo[db] = tr_op<D>(dt1, lane, db, 1);
-        uq[db] = tr_op<D>(qt1, lane, db, 1);
+        udo[db] = tr_at(ta[db], T::BYTES + 16 * T::ROWB);
+        uq[db] = tr_at(ta[db], 16 * T::ROWB);
       }
 #pragma unroll
       for (int db = H1; db < T::NDB; ++db) {
@@ -461,6 +493,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const float dq_row = q < Nq ? Dv[(size_t)bh * Nq + q] : 0.f;
   f32x16 acc[T::NDB];
   zero_acc(acc);
+  const OpOffsets<D> oo = op_offsets<D>(lane);
 
   // K and V blocks go from memory straight into LDS (no staging registers):
   // copy i of a wave fills tile bytes 1024 (wave IPW + i) .. +1023, lane l
@@ -510,8 +543,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       bf16x8 ka[T::KS], va[T::KS];
 #pragma unroll
       for (int s = 0; s < KH; ++s) {
-        ka[s] = row_op<D>(kt_, lane, s);
-        va[s] = row_op<D>(vt, lane, s);
+        const uint32_t a = lane_addr(kt_, oo.row[s]);
+        ka[s] = row_at(a, 0);
+        va[s] = row_at(a, T::BYTES);  // the V tile follows the K tile
       }
       f32x16 S, dP;
       mm_first(S, ka[0], qf[0]);
@@ -522,8 +556,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         after_products(k0, v0);
 #pragma unroll
         for (int s = KH; s < T::KS; ++s) {
-          ka[s] = row_op<D>(k0, lane, s);
-          va[s] = row_op<D>(v0, lane, s);
+          const uint32_t a = lane_addr(k0, oo.row[s]);
+          ka[s] = row_at(a, 0);
+          va[s] = row_at(a, T::BYTES);
         }
       }
 #pragma unroll
@@ -532,9 +567,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         mm_next(dP, va[s], df[s]);
       }
       // transposed K operands of the block's first 16 keys, read during the wait
+      uint32_t ta[T::NDB][2];
       bf16x8 tk[T::NDB];
 #pragma unroll
-      for (int db = 0; db < T::NDB; ++db) tk[db] = tr_op<D>(kt_, lane, db, 0);
+      for (int db = 0; db < T::NDB; ++db) {
+        ta[db][0] = lane_addr(kt_, oo.tr[db][0]);
+        ta[db][1] = lane_addr(kt_, oo.tr[db][1]);
+        tk[db] = tr_at(ta[db], 0);
+      }
       pause_scores(S, dP);
       const int k0 = kb * kRows;
       float dS[16];
@@ -565,12 +605,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       constexpr int H1 = T::NDB / 2;
 #pragma unroll
       for (int db = 0; db < H1; ++db) mm_acc(acc[db], tk[db], sb[0]);
-      const lds_char* k1 = kt_;
-      const lds_char* v1 = vt;
-      after_products(k1, v1);
+      after_products(ta);
       bf16x8 uk[T::NDB];
 #pragma unroll
-      for (int db = 0; db < T::NDB; ++db) uk[db] = tr_op<D>(k1, lane, db, 1);
+      for (int db = 0; db < T::NDB; ++db) uk[db] = tr_at(ta[db], 16 * T::ROWB);
 #pragma unroll
       for (int db = H1; db < T::NDB; ++db) mm_acc(acc[db], tk[db], sb[0]);
 #pragma unroll
