@@ -344,7 +344,7 @@ def main():
                                         "single": round(ds_gbps / PEAK_HBM_GBPS, 4),
                                         "paged_batched": round(pg_gbps / PEAK_HBM_GBPS, 4)},
                    "read_ceiling": {"128MiB": round(ceil_small, 1), "8GiB": round(ceil_big, 1),
-                                    "kind": "plain 16-byte-load read kernel, cold clean cache"},
+                                    "kind": "plain non-temporal 16-byte-load read kernel, cold clean cache"},
                    "frac_of_read_ceiling": {"batched": round(db_gbps / ceil_big, 4),
                                             "single": round(ds_gbps / ceil_small, 4),
                                             "paged_batched": round(pg_gbps / ceil_big, 4)}},

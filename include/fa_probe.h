@@ -20,7 +20,7 @@ extern "C" {
 
 /*
  * Reads `bytes` bytes at `src` (device, 16-byte aligned, bytes a positive
- * multiple of 16) with 16-byte loads, 256 KB per 256-thread workgroup, eight
+ * multiple of 16) with non-temporal 16-byte loads, 256 KB per 256-thread workgroup, eight
  * loads in flight per lane, and keeps nothing: `sink` (device, >= 4 bytes,
  * owned by the caller) is written only if the XOR of the data equals a fixed
  * constant, so the loads cannot be dropped.  Enqueued on `stream`; returns

@@ -13,6 +13,8 @@ using fa::u32x4;
 constexpr int kThreads = 256;
 constexpr int kPerWg16 = 256 * 1024 / 16;  // 16-byte words per workgroup
 constexpr int kInFlight = 8;               // loads in flight per lane
+// Each byte is read once, so the loads carry the non-temporal hint, as the
+// decode kernel's cache reads do.
 
 __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ p, size_t n16,
                                                         unsigned* __restrict__ sink) {
@@ -23,7 +25,7 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) {
       const size_t idx = base + i + (size_t)k * kThreads;
-      v[k] = idx < n16 ? p[idx] : u32x4{0u, 0u, 0u, 0u};
+      v[k] = idx < n16 ? __builtin_nontemporal_load(p + idx) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) acc ^= v[k];
