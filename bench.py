@@ -1,6 +1,7 @@
 """Benchmark of the exact-attention forward path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-budget SECONDS]
+    python bench.py --sweep-seqlen
 
 One step is one pass of the whole hot path over resident synthetic inputs:
   1. fa_fwd      causal prefill, B=1, H=32, Nq=Nk=8192, d=128, bf16
@@ -27,6 +28,11 @@ rates (GB/s) ride along in `decode`, beside the read rate a plain streaming
 read kernel reaches on the same byte counts (the empirical ceiling); `roofline` describes the prefill kernel
 against the bf16 dense matrix-core peak; `cpu_baseline` times the fp64 oracle
 on a bounded sample of the prefill on the host.
+
+`--sweep-seqlen` instead times the prefill (d=128 with H=32, d=64 with H=16,
+non-causal and causal) and the d=128 backward at sequence lengths 512 ..
+32768 with the batch chosen so that every launch holds 32768 tokens, and
+prints one JSON line per shape.
 """
 from __future__ import annotations
 
@@ -57,7 +63,63 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--cpu-budget", type=float, default=12.0,
                    help="seconds of host time for the oracle baseline sample")
+    p.add_argument("--sweep-seqlen", action="store_true",
+                   help="time prefill and backward against sequence length instead")
     return p.parse_args()
+
+
+SWEEP_TOKENS = 32768
+SWEEP_LENGTHS = (512, 1024, 2048, 4096, 8192, 16384, 32768)
+
+
+def sweep_seqlen(fa, W, dev):
+    """TFLOP/s of the prefill and the d=128 backward against sequence length
+    at a fixed 32768 tokens per launch (B = 32768 / N), seeded N(0,1) inputs,
+    the mean of HIP-event times on the launch stream after warm-up calls."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+
+    def mean_ms(fn, reps, skip):
+        ts = []
+        for i in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            if i >= skip:
+                ts.append(e0.elapsed_time(e1))
+        return statistics.mean(ts)
+
+    for d, H in ((128, 32), (64, 16)):
+        for N in SWEEP_LENGTHS:
+            B = SWEEP_TOKENS // N
+            scale = d ** -0.5
+            q, k, v = W.prefill_inputs(B, H, N, N, d, "bf16", seed=7, device=dev)
+            o = torch.empty_like(q)
+            lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+            rec = {"d": d, "H": H, "B": B, "N": N, "unit": "TFLOP/s"}
+            for causal in (False, True):
+                ms = mean_ms(lambda: fa.fa_fwd(q, k, v, scale, causal, out=o, lse=lse), 20, 5)
+                flops = 4 * B * H * N * N * d / (2 if causal else 1)
+                rec["fwd_causal" if causal else "fwd"] = round(flops / (ms * 1e-3) / 1e12, 1)
+            if d == 128:
+                dout = W.prefill_inputs(B, H, N, N, d, "bf16", seed=8, device=dev)[0]
+                ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=dev)
+                dq = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
+                dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+                for causal in (False, True):
+                    fa.fa_fwd(q, k, v, scale, causal, out=o, lse=lse)
+                    ms = mean_ms(lambda: fa.fa_bwd(q, k, v, o, dout, lse, scale, causal, dq=dq,
+                                                   dk=dk, dv=dv, workspace=ws), 12, 3)
+                    flops = 2.5 * 4 * B * H * N * N * d / (2 if causal else 1)
+                    rec["bwd_causal" if causal else "bwd"] = round(flops / (ms * 1e-3) / 1e12, 1)
+                del dout, ws, dq, dk, dv
+            print(json.dumps(rec), flush=True)
+            del q, k, v, o, lse
+            torch.cuda.empty_cache()
 
 
 def cpu_baseline(budget_s: float):
@@ -140,6 +202,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+    if args.sweep_seqlen:
+        sweep_seqlen(fa, W, dev)
+        return
 
     P = W.LONG_PREFILL
     DB = W.DECODE_BATCHED

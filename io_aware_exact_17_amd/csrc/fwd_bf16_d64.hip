@@ -195,25 +195,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int end = CAUSAL ? min(Nk, q0_of(it) + wave * 32 + 32 + Nk - Nq_of(it)) : Nk;
     return end > 0 ? (end + BC - 1) / BC : 0;
   };
-  // A stream position: key tile j of this workgroup's item `item`, which
-  // spans n_pos = max(n_tiles, 1) positions.  item >= n_items ends the stream.
+  // Round r of the stream gives workgroup g item r*G + g on even rounds and
+  // r*G + G-1-g on odd ones.  Items are numbered heaviest first, so the
+  // reversed direction pairs a round's heaviest item with the next round's
+  // lightest: with fewer items per query-tile level than workgroups (one
+  // long causal sequence over few heads), a plain stride would hand the low
+  // workgroups the heaviest item of every round.  Past the end: n_items.
+  auto slot = [&](int r) -> int {
+    const long long i = (long long)r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    return i < n_items ? (int)i : n_items;
+  };
+  // A stream position: key tile j of this workgroup's item `item` (round
+  // r), which spans n_pos = max(n_tiles, 1) positions.  item >= n_items ends
+  // the stream.
   struct Cursor {
-    int item, j, n_pos;
+    int r, item, j, n_pos;
     Item it;  // the item's description (valid while item < n_items)
   };
-  auto settle = [&](Cursor& cu) {  // move to the first non-empty item at or after cu.item
-    while (cu.item < n_items && !item_info(cu.item, cu.it)) cu.item += G;
+  auto settle = [&](Cursor& cu) {  // move to the first non-empty item at or after round cu.r
+    while (cu.item < n_items && !item_info(cu.item, cu.it)) cu.item = slot(++cu.r);
     cu.j = 0;
     cu.n_pos = cu.item < n_items ? max(n_tiles_of(cu.it), 1) : 0;
   };
   auto advance = [&](Cursor& cu) {
     if (++cu.j < cu.n_pos) return;
-    cu.item += G;
+    cu.item = slot(++cu.r);
     settle(cu);
   };
 
   Cursor cur;
-  cur.item = (int)blockIdx.x;
+  cur.r = 0;
+  cur.item = slot(0);
   settle(cur);
   if (cur.item >= n_items) return;  // uniform: no work for this workgroup
 
@@ -239,7 +251,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   auto prefetch_q = [&](const Cursor& cu) {
     if (cu.j != cu.n_pos - 1) return;
     Cursor nx;
-    nx.item = cu.item + G;
+    nx.r = cu.r + 1;
+    nx.item = slot(nx.r);
     settle(nx);
     if (nx.item < n_items) load_q(nx.it, qn);
   };
