@@ -46,8 +46,8 @@
 //    happens on the first tile and rarely afterwards; the mathematics is
 //    unchanged because the final division uses the same reference.
 //  * Work items (head, query tile) are listed heaviest query tile first,
-//    heads fastest.  Dense runs one workgroup per CU, each walking every
-//    G-th item as one stream (see the kernel); since workgroups are dealt
+//    heads fastest.  Dense runs one workgroup per CU, each taking one item
+//    per round of G as one stream (see the kernel); since workgroups are dealt
 //    round-robin to the 8 XCDs, when G (the CU count, 256, once there are
 //    that many items) and B*H are multiples of 8 every item of a head lands
 //    on the same XCD and shares its K/V in that XCD's L2.
@@ -99,8 +99,9 @@ __device__ __forceinline__ int swz64(int r, int c) {
 }
 
 // The work is a list of items, one per (sequence or batch-head, query tile),
-// heaviest query tile first and heads fastest.  Workgroup g takes items g,
-// g + G, g + 2G, ... (G = number of workgroups) and walks them as one stream
+// heaviest query tile first and heads fastest.  Workgroup g takes one item
+// per round of G (G = number of workgroups; odd rounds in reverse order of
+// 8-workgroup blocks, which balances causal work) and walks them as one stream
 // of positions, one per key tile of each item in turn (an item with no
 // visible key still takes one position, for its epilogue).  The staging of
 // tiles two positions ahead, the lag of wave group B and the fetch of the
@@ -195,14 +196,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int end = CAUSAL ? min(Nk, q0_of(it) + wave * 32 + 32 + Nk - Nq_of(it)) : Nk;
     return end > 0 ? (end + BC - 1) / BC : 0;
   };
-  // Round r of the stream gives workgroup g item r*G + g on even rounds and
-  // r*G + G-1-g on odd ones.  Items are numbered heaviest first, so the
-  // reversed direction pairs a round's heaviest item with the next round's
-  // lightest: with fewer items per query-tile level than workgroups (one
-  // long causal sequence over few heads), a plain stride would hand the low
-  // workgroups the heaviest item of every round.  Past the end: n_items.
+  // Round r of the stream gives workgroup g item r*G + g on even rounds;
+  // odd rounds run the round backwards in blocks of 8 workgroups (item
+  // r*G + G-8 - (g & ~7) + (g & 7)), so g mod 8, and with it the XCD that
+  // holds a head's K/V, stays the same (plain G-1-g when G is not a multiple
+  // of 8).  Items are numbered heaviest first, so the reversed direction
+  // pairs a round's heavy items with the next round's light ones: with fewer
+  // items per query-tile level than workgroups (one long causal sequence
+  // over few heads), a plain stride would hand the low workgroups the
+  // heaviest item of every round.  Past the end: n_items.
+  const int g_rev = (G & 7) == 0 ? G - 8 - ((int)blockIdx.x & ~7) + ((int)blockIdx.x & 7)
+                                 : G - 1 - (int)blockIdx.x;
   auto slot = [&](int r) -> int {
-    const long long i = (long long)r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    const long long i = (long long)r * G + ((r & 1) ? g_rev : (int)blockIdx.x);
     return i < n_items ? (int)i : n_items;
   };
   // A stream position: key tile j of this workgroup's item `item` (round
