@@ -138,13 +138,15 @@ def pin_shift(impl):
 
 
 def pin_online(impl):
-    """The streaming (m, l, u) recurrence of the pages reaches the same result."""
+    """The streaming (m, l, u) evaluation of the pages reaches the same result,
+    key by key (the running recurrence) and in blocks of 3 (tiles + merge)."""
     for Nq, Nk, causal in [(7, 7, True), (5, 11, True), (11, 5, True), (6, 9, False)]:
         q, k, v = rand((2, 2, Nq, 8), 61) * 3, rand((2, 2, Nk, 8), 62) * 3, rand((2, 2, Nk, 4), 63)
         O, L = attn(impl, q, k, v, 0.4, causal)
-        Oo, Lo = online.online_attention(q, k, v, 0.4, causal)
-        close(O, Oo)
-        close(L, Lo)
+        for block in (1, 3):
+            Oo, Lo = online.streamed_attention(q, k, v, 0.4, causal, block=block)
+            close(O, Oo)
+            close(L, Lo)
 
 
 def pin_sdpa(impl):
@@ -175,12 +177,16 @@ def test_oracle_pin(pin):
 
 
 # ------------------------------------------------- online / merge pins
+def _row(x):
+    return np.asarray(x, dtype=np.float64)[None, :]
+
+
 def test_online_worked_example():
     g = json.load(open(GOLDEN))
-    st = online.online_row(g["scores"], g["values"])
-    o, lse = online.finish(st)
-    close(o, float(g["O"]))
-    close(lse, float(g["LSE"]))
+    st = online.per_key(_row(g["scores"]), np.asarray(g["values"], dtype=np.float64))
+    o, lse = online.normalise(st)
+    close(o[0, 0], float(g["O"]))
+    close(lse[0], float(g["LSE"]))
     # a naive exp without the max shift overflows, which is why the shift exists
     with np.errstate(over="ignore"):
         assert np.isinf(np.exp(np.float64(1000.0)))
@@ -188,14 +194,21 @@ def test_online_worked_example():
 
 def test_merge_worked_example():
     g = json.load(open(GOLDEN))
-    s, v = g["scores"], g["values"]
-    left = online.summarize(s[:2], v[:2])
-    right = online.summarize(s[2:], v[2:])
-    close(left, [float(x) for x in g["left_state"]])
-    close(right, [float(x) for x in g["right_state"]])
-    merged = online.merge(left, right)
-    close(merged, [float(x) for x in g["merged_state"]])
-    close(merged[2] / merged[1], float(g["merged_O"]))
+    s, v = _row(g["scores"]), np.asarray(g["values"], dtype=np.float64)
+
+    def flat(st):
+        return [st[0][0], st[1][0], st[2][0, 0]]
+
+    left = online.block_state(s[:, :2], v[:2])
+    right = online.block_state(s[:, 2:], v[2:])
+    close(flat(left), [float(x) for x in g["left_state"]])
+    close(flat(right), [float(x) for x in g["right_state"]])
+    merged = online.combine(left, right)
+    close(flat(merged), [float(x) for x in g["merged_state"]])
+    close(merged[2][0, 0] / merged[1][0], float(g["merged_O"]))
+    # the same split through the scan, and the per-key scan
+    close(flat(online.scan(s, v, [2])), [float(x) for x in g["merged_state"]])
+    close(online.normalise(online.per_key(s, v))[0][0, 0], float(g["merged_O"]))
 
 
 def test_merge_invariance_every_split():
@@ -207,23 +220,23 @@ def test_merge_invariance_every_split():
         s = rng.standard_normal(n) * (1 + 300 * (trial % 2))
         v = rng.standard_normal((n, dv))
         O, L = ref.head_attention(np.ones((1, 1)), s[:, None], v, 1.0)
+        sr = s[None, :]
         for cut in range(1, n):
-            st = online.merge(online.summarize(s[:cut], v[:cut]), online.summarize(s[cut:], v[cut:]))
-            o, lse = online.finish(st)
-            close(o, O[0], 1e-12 * max(1, np.abs(O).max()))
-            close(lse, L[0], 1e-12 * max(1.0, abs(L[0])))
+            o, lse = online.normalise(online.scan(sr, v, [cut]))
+            close(o[0], O[0], 1e-12 * max(1, np.abs(O).max()))
+            close(lse[0], L[0], 1e-12 * max(1.0, abs(L[0])))
         for _ in range(5):
             k = int(rng.integers(2, min(n, 8) + 1))
             cuts = np.sort(rng.choice(np.arange(1, n), size=k - 1, replace=False))
             parts = np.split(np.arange(n), cuts)
-            states = [online.summarize(s[p], v[p]) for p in parts]
+            states = [online.block_state(sr[:, p], v[p]) for p in parts]
             order = rng.permutation(len(states))  # merge order must not matter
             st = states[order[0]]
             for j in order[1:]:
-                st = online.merge(st, states[j])
-            o, lse = online.finish(st)
-            close(o, O[0], 1e-12 * max(1, np.abs(O).max()))
-            close(lse, L[0], 1e-12 * max(1.0, abs(L[0])))
+                st = online.combine(st, states[j])
+            o, lse = online.normalise(st)
+            close(o[0], O[0], 1e-12 * max(1, np.abs(O).max()))
+            close(lse[0], L[0], 1e-12 * max(1.0, abs(L[0])))
 
 
 # ---------------------------------------------------- conventions
@@ -482,6 +495,87 @@ def test_grad_planted_mistakes_are_caught():
     }
     for name, (g, which) in slips.items():
         assert not np.allclose(g, want[which], atol=1e-6), name
+
+
+def _torch_grads_batched(q, k, v, do, scale, causal):
+    """dQ, dK, dV of sum(O * dO) for whole [B, H, N, d] tensors by float64
+    torch autograd (batched products, no per-head loop)."""
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    S = float(np.float32(scale)) * qt @ kt.transpose(-1, -2)
+    Nq, Nk = q.shape[2], k.shape[2]
+    if causal:
+        S = S.masked_fill(torch.arange(Nk)[None, :] > (torch.arange(Nq) + (Nk - Nq))[:, None],
+                          -float("inf"))
+    P = torch.softmax(S, -1).nan_to_num(0.0)
+    (P @ vt * torch.tensor(do)).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def pin_attention_grad(impl):
+    """The [B, H] gradient wrapper: every (b, h) slice against batched float64
+    autograd, with heads that differ (distinct scales per head) so a mixed-up
+    slice or a swapped dK / dV (d == dv here) cannot pass."""
+    rng = np.random.default_rng(17)
+    B, H, d = 2, 3, 5
+    for causal, Nq, Nk in [(False, 6, 9), (True, 6, 9), (True, 9, 6), (False, 4, 4)]:
+        spread = (1.0 + np.arange(B * H).reshape(B, H, 1, 1)) / 3
+        q = rng.standard_normal((B, H, Nq, d)) * spread
+        k = rng.standard_normal((B, H, Nk, d))
+        v = rng.standard_normal((B, H, Nk, d)) + spread
+        do = rng.standard_normal((B, H, Nq, d))
+        want = _torch_grads_batched(q, k, v, do, 0.45, causal)
+        got = impl(q, k, v, do, 0.45, causal)
+        for g, w in zip(got, want):
+            close(g, w, 1e-12)
+
+
+def test_attention_grad_wrapper_pin():
+    pin_attention_grad(oracle.attention_grad)
+
+
+def test_attention_grad_wrapper_head_subset():
+    """Only the listed (b, h) pairs are evaluated; they equal the full call."""
+    rng = np.random.default_rng(18)
+    q, k, v, do = (rng.standard_normal((2, 3, 5, 4)) for _ in range(4))
+    full = oracle.attention_grad(q, k, v, do, 0.3, True)
+    part = oracle.attention_grad(q, k, v, do, 0.3, True, heads=[(1, 2), (0, 1)])
+    for f, g in zip(full, part):
+        for b, h in [(1, 2), (0, 1)]:
+            assert np.array_equal(f[b, h], g[b, h])
+        assert np.isnan(g[0, 0]).all() and np.isnan(g[1, 1]).all()
+
+
+def test_attention_grad_wrapper_planted_mistakes_are_caught():
+    """Slips in the [B, H] wrapper (planted here, on the CPU) fail its pin."""
+    def swapped_dk_dv(q, k, v, do, scale, causal):
+        dq, dk, dv = oracle.attention_grad(q, k, v, do, scale, causal)
+        return dq, dv, dk
+
+    def next_head_keys(q, k, v, do, scale, causal):
+        B, H = q.shape[:2]
+        out = [np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)]
+        for b in range(B):
+            for h in range(H):
+                g = ref.head_attention_grad(q[b, h], k[b, (h + 1) % H], v[b, h], do[b, h], scale,
+                                            causal)
+                for o, x in zip(out, g):
+                    o[b, h] = x
+        return out
+
+    def batch_index_mixed(q, k, v, do, scale, causal):
+        B, H = q.shape[:2]
+        out = [np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)]
+        for b in range(B):
+            for h in range(H):
+                g = ref.head_attention_grad(q[b, h], k[b, h], v[B - 1 - b, h], do[b, h], scale,
+                                            causal)
+                for o, x in zip(out, g):
+                    o[b, h] = x
+        return out
+
+    for slip in (swapped_dk_dv, next_head_keys, batch_index_mixed):
+        with pytest.raises(AssertionError):
+            pin_attention_grad(slip)
 
 
 # ---------------------------------------------------------- block sparsity
