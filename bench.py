@@ -122,6 +122,95 @@ def sweep_seqlen(fa, W, dev):
             torch.cuda.empty_cache()
 
 
+def blas_threads():
+    """Threads of the BLAS library NumPy calls (the oracle's products)."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max(i.get("num_threads", 1) for i in threadpool_info())
+    except Exception:
+        import torch
+
+        return torch.get_num_threads()
+
+
+def oracle_per_config(budget_s: float, dev, decode_batched):
+    """The oracle timed on bounded samples of the other workloads, on the
+    host, after the GPU timing: the tiny fp32 case whole, whole heads of the
+    GPT-2-medium shape (non-causal) until the budget, the single decode whole,
+    and whole sequences (all heads) of the batched decode until the budget.
+    Inputs are copied to the host before the clock starts."""
+    import torch
+
+    import oracle
+    import workloads as W
+
+    out = {}
+    s = W.TINY_F32
+    q, k, v = W.prefill_spec_inputs(s, "cpu")
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, s.scale, s.causal)
+    dt = time.perf_counter() - t0
+    out["tiny_f32"] = {"s": round(dt, 4), "GFLOP/s": round(s.flops() / dt / 1e9, 3)}
+
+    G = W.GPT2M
+    g = torch.Generator().manual_seed(G.seed)
+    heads, t_tot = 0, 0.0
+    while heads == 0 or t_tot < budget_s:
+        qh, kh, vh = (torch.randn(G.Nq, G.d, generator=g).to(torch.bfloat16) for _ in range(3))
+        t0 = time.perf_counter()
+        oracle.head_attention(qh, kh, vh, G.scale, causal=False)
+        t_tot += time.perf_counter() - t0
+        heads += 1
+    out["gpt2_medium_noncausal"] = {
+        "GFLOP/s": round(heads * 4.0 * G.Nq * G.Nk * G.d / t_tot / 1e9, 2),
+        "sample": f"{heads} whole heads of {G.B * G.H}, {t_tot:.2f} s"}
+
+    S = W.DECODE_SINGLE
+    q, kc, vc, sl, off = W.decode_spec_inputs(S, "cpu")
+    t0 = time.perf_counter()
+    oracle.decode(q, kc, vc, sl, off, S.scale)
+    dt = time.perf_counter() - t0
+    out["decode_single"] = {"GB/s": round(W.decode_kv_bytes(sl, S.H, S.d) / dt / 1e9, 3),
+                            "s": round(dt, 3), "sample": "whole workload"}
+
+    D = W.DECODE_BATCHED
+    dq, dk, dv, dl, do = decode_batched
+    lens = dl.cpu()
+    offs = do.cpu()
+    seqs, t_tot, nbytes = 0, 0.0, 0
+    while seqs < D.B and (seqs == 0 or t_tot < budget_s):
+        lo, n = int(offs[seqs]), int(lens[seqs])
+        kh, vh = dk[lo:lo + n].cpu(), dv[lo:lo + n].cpu()
+        qh = dq[seqs:seqs + 1].cpu()
+        one = torch.tensor([n], dtype=torch.int32)
+        zero = torch.zeros(1, dtype=torch.int32)
+        t0 = time.perf_counter()
+        oracle.decode(qh, kh, vh, one, zero, D.scale)
+        t_tot += time.perf_counter() - t0
+        nbytes += W.decode_kv_bytes(one, D.H, D.d)
+        seqs += 1
+    out["decode_batched"] = {"GB/s": round(nbytes / t_tot / 1e9, 3),
+                             "sample": f"{seqs} of {D.B} whole sequences, all heads, {t_tot:.2f} s"}
+    out["cores"] = len(os.sched_getaffinity(0))
+    out["blas_threads"] = blas_threads()
+    return out
+
+
+def sclk_mhz():
+    """The current shader clock level from sysfs (None where not readable)."""
+    import glob
+
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path):
+                if line.strip().endswith("*"):
+                    return int(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
 def cpu_baseline(budget_s: float):
     """The fp64 oracle (as it stands) on whole heads of the causal prefill
     workload, one head at a time until the budget is spent (at least one)."""
@@ -131,12 +220,7 @@ def cpu_baseline(budget_s: float):
     import oracle
     import workloads as W
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max(i.get("num_threads", 1) for i in threadpool_info())
-    except Exception:
-        threads = torch.get_num_threads()
+    threads = blas_threads()
     s = W.LONG_PREFILL
     g = torch.Generator().manual_seed(s.seed)
     heads = 0
@@ -153,7 +237,8 @@ def cpu_baseline(budget_s: float):
         flops += 4.0 * s.Nq * s.Nk * s.d / 2
         if heads >= s.H:
             break
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s",
+            "cores": len(os.sched_getaffinity(0)), "blas_threads": int(threads),
             "kind": "oracle",
             "sample": f"{heads} of {s.H} heads of the causal N=8192 d=128 prefill, whole heads, "
                       f"fp64 NumPy with S and P materialised; {t_total:.1f} s"}
@@ -218,14 +303,16 @@ def main():
     db_out = torch.empty_like(dbq)
     db_lse = torch.empty(DB.B, DB.H, dtype=torch.float32, device=dev)
     db_sk = fa.fa_decode_split_keys(DB.B, DB.H, DB.d, DB.max_len)
-    db_ws = torch.empty(fa.fa_decode_workspace_bytes(DB.B, DB.H, DB.d, DB.max_len, 0),
+    # decode workspaces: zero-filled once (their arrival counters start at 0
+    # and every call leaves them at 0)
+    db_ws = torch.zeros(fa.fa_decode_workspace_bytes(DB.B, DB.H, DB.d, DB.max_len),
                         dtype=torch.uint8, device=dev)
 
     dsq, dsk, dsv, dsl, dso = W.decode_spec_inputs(DS, dev)
     ds_out = torch.empty_like(dsq)
     ds_lse = torch.empty(DS.B, DS.H, dtype=torch.float32, device=dev)
     ds_sk = fa.fa_decode_split_keys(DS.B, DS.H, DS.d, DS.max_len)
-    ds_ws = torch.empty(fa.fa_decode_workspace_bytes(DS.B, DS.H, DS.d, DS.max_len, 0),
+    ds_ws = torch.zeros(fa.fa_decode_workspace_bytes(DS.B, DS.H, DS.d, DS.max_len),
                         dtype=torch.uint8, device=dev)
 
     # The batched workload again as a paged cache (16-token pages, random order).
@@ -235,7 +322,7 @@ def main():
     pg_v = W.to_pages(dbv, dbl, dbo, pg_bt, PAGE, pg_pages)
     pg_bt = pg_bt.to(dev)
     pg_sk = fa.fa_decode_paged_split_keys(DB.B, DB.H, DB.d, DB.max_len, PAGE)
-    pg_ws = torch.empty(fa.fa_decode_workspace_bytes(DB.B, DB.H, DB.d, DB.max_len, pg_sk),
+    pg_ws = torch.zeros(fa.fa_decode_split_workspace_bytes(DB.B, DB.H, DB.d, DB.max_len, pg_sk),
                         dtype=torch.uint8, device=dev)
     pg_out = torch.empty_like(dbq)
     pg_lse = torch.empty(DB.B, DB.H, dtype=torch.float32, device=dev)
@@ -287,10 +374,10 @@ def main():
         e0.record(stream)
         fa.fa_fwd(q, k, v, P.scale, True, out=o, lse=lse)
         e1.record(stream)
-        fa.fa_decode_varlen(dbq, dbk, dbv, dbl, dbo, DB.max_len, DB.scale, 0, out=db_out,
+        fa.fa_decode_varlen(dbq, dbk, dbv, dbl, dbo, DB.max_len, DB.scale, out=db_out,
                             lse=db_lse, workspace=db_ws)
         e2.record(stream)
-        fa.fa_decode_varlen(dsq, dsk, dsv, dsl, dso, DS.max_len, DS.scale, 0, out=ds_out,
+        fa.fa_decode_varlen(dsq, dsk, dsv, dsl, dso, DS.max_len, DS.scale, out=ds_out,
                             lse=ds_lse, workspace=ds_ws)
         e3.record(stream)
         fa.fa_decode_paged(dbq, pg_k, pg_v, pg_bt, dbl, DB.max_len, DB.scale, 0, out=pg_out,
@@ -351,7 +438,9 @@ def main():
 
     ceil_small, ceil_big = read_ceiling(torch, fa, dev, stream, ds_bytes)
 
+    max_alloc = torch.cuda.max_memory_allocated(dev)
     cpu = cpu_baseline(args.cpu_budget)
+    per_cfg = oracle_per_config(min(3.0, args.cpu_budget / 4), dev, (dbq, dbk, dbv, dbl, dbo))
 
     line = {
         "metric": METRIC,
@@ -434,9 +523,25 @@ def main():
                      "frac_of_bf16_peak": round(bw_tflops / PEAK_BF16_TFLOPS, 4),
                      "flops_convention": "2.5 x forward (five products of 2*N*N*d, halved causal)"},
         "cpu_baseline": cpu,
+        "oracle_per_config": per_cfg,
+        "memory": {"max_allocated_bytes": int(max_alloc),
+                   "workspace_bytes": {"decode_batched": db_ws.numel(),
+                                       "decode_single": ds_ws.numel(),
+                                       "decode_paged": pg_ws.numel(),
+                                       "backward": bw_ws.numel()},
+                   "note": "every buffer is allocated by the caller (torch); the library "
+                           "allocates no device memory"},
+        "dispatch": {"fa_fwd d=128 causal": "fwd_bf16_kernel<128, true, false, false>",
+                     "fa_fwd d=64": "fwd_bf16_kernel<64, causal, false> (fwd_bf16_d64.hip)",
+                     "fa_decode_varlen / fa_decode_paged": "decode_split_kernel<128, paged, fused=true>",
+                     "fa_fwd_varlen": "fwd_bf16_kernel<128, true, true, false>",
+                     "fa_fwd_block_sparse": "fwd_bf16_kernel<128, true, false, true>",
+                     "fa_bwd": "bwd_rows_kernel, bwd_dkdv_kernel, bwd_dq_kernel",
+                     "library": fa.LIB_PATH.replace(ROOT + os.sep, ""),
+                     "fallback": "none (the binding raises if the library is missing)"},
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "torch": torch.__version__,
-                   "hip": torch.version.hip},
+                   "hip": torch.version.hip, "sclk_mhz_at_end": sclk_mhz()},
     }
     print(json.dumps(line), flush=True)
 

@@ -85,8 +85,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            hipStream_t stream);
 
 /*
- * Same contract with fp32 q, k, v, o.  Arithmetic is plain fp32 throughout
- * (no reduced-precision products).
+ * Same contract with fp32 q, k, v, o: the explainer's §1 definition and §2
+ * running-state recurrence evaluated in plain fp32 throughout (no
+ * reduced-precision products), so the result differs from the exact one only
+ * by fp32 rounding.  A parity kernel, not a fast path.
  */
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int Nq, int Nk, int d, float scale, int causal,
@@ -167,11 +169,12 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 /*
  * Decode: one new query per sequence over a packed, variable-length KV cache
  * (explainer §6: a single query sees its whole history; batched decode mixes
- * history lengths).  Each sequence's keys are cut into chunks of `split_keys`
- * keys that are processed in parallel; each chunk leaves a partial state
- * (m, l, u) in the workspace and a second kernel merges the partial states of
- * a sequence with the block-merge rule of explainer §3/§7 (a sequence that
- * fits in one chunk is finished by the first kernel).
+ * history lengths).  Each sequence's keys are cut into chunks that are
+ * processed in parallel; each chunk leaves a partial state (m, l, u) in the
+ * workspace, and the chunk of a sequence that finishes last merges its
+ * sequence's states with the block-merge rule of explainer §3/§7 (a sequence
+ * that fits in one chunk is finished on the spot; shapes beyond the fused
+ * merge's limits get a second, merging kernel instead).
  *
  *   q        bf16 [B, H, d]        (device)
  *   kcache   bf16 [T, H, d]        token-major (device)
@@ -184,24 +187,52 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  *   lse      fp32 [B, H]           written (device)
  *   max_seqlen  an upper bound of seqlens[] (host; sizes the grid, so no
  *               device-to-host copy is needed); 0 <= seqlens[b] <= max_seqlen
- *   split_keys  keys per chunk, a positive multiple of 64 giving at most 256
- *               chunks for max_seqlen, or 0 to let the library choose
- *               (fa_decode_split_keys)
- *   workspace   device scratch of at least fa_decode_workspace_bytes(...) bytes,
- *               owned by the caller; its contents need no initialisation.
- *               Calls that run at the same time must not share a workspace.
+ *   workspace   device scratch of at least fa_decode_workspace_bytes(B, H, d,
+ *               max_seqlen) bytes, owned by the caller.  Its first 65536 bytes
+ *               are arrival counters: they must be ZERO before the first call
+ *               that uses the workspace (zero-fill it once after allocating
+ *               it: hipMemset, torch.zeros), and every call leaves them zero
+ *               again when it completes, so a workspace can serve any number
+ *               of later calls, of any shape, without clearing.  The rest
+ *               needs no initialisation.  Calls that run at the same time must
+ *               not share a workspace.
  *
  * A sequence with seqlens[b] == 0 gets O = 0 and LSE = -inf.  Cache row
  * addresses are computed in 64-bit, so T * H * d may exceed 2^31.
+ * fa_decode_workspace_bytes returns 0 for invalid arguments.
  */
-int fa_decode_split_keys(int B, int H, int d, int max_seqlen);
-size_t fa_decode_workspace_bytes(int B, int H, int d, int max_seqlen, int split_keys);
+size_t fa_decode_workspace_bytes(int B, int H, int d, int max_seqlen);
 int fa_decode_varlen(const void* q, const void* kcache, const void* vcache,
                      const int32_t* seqlens, const int32_t* offsets,
                      void* o, float* lse,
-                     int B, int H, int d, int max_seqlen, float scale, int split_keys,
+                     int B, int H, int d, int max_seqlen, float scale,
                      void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
+
+/*
+ * The chunk size fa_decode_varlen picks (keys per chunk): 256, doubled while
+ * the grid would exceed 16384 workgroups or a sequence 256 chunks.  0 for
+ * invalid arguments.
+ */
+int fa_decode_split_keys(int B, int H, int d, int max_seqlen);
+
+/*
+ * fa_decode_varlen with the chunk size given (for tuning and tests): the same
+ * contract, plus
+ *   split_keys  keys per chunk, a positive multiple of 64 giving at most 4096
+ *               chunks for max_seqlen (FA_ERR_INVALID_ARG otherwise)
+ *   workspace   at least fa_decode_split_workspace_bytes(B, H, d, max_seqlen,
+ *               split_keys) bytes, with the same counter rule
+ * fa_decode_split_workspace_bytes(..., 0) equals fa_decode_workspace_bytes;
+ * it returns 0 for invalid arguments.
+ */
+size_t fa_decode_split_workspace_bytes(int B, int H, int d, int max_seqlen, int split_keys);
+int fa_decode_varlen_split(const void* q, const void* kcache, const void* vcache,
+                           const int32_t* seqlens, const int32_t* offsets,
+                           void* o, float* lse,
+                           int B, int H, int d, int max_seqlen, float scale, int split_keys,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /*
  * Decode over a paged KV cache (explainer §6 names paging as the concern of
@@ -218,19 +249,22 @@ int fa_decode_varlen(const void* q, const void* kcache, const void* vcache,
  *                (an entry outside reads page num_pages - 1 instead of
  *                faulting; later entries are never read)
  *   seqlens      int32 [B]                              (device)
- *   o, lse, max_seqlen, scale, workspace: as for fa_decode_varlen (the same
- *                fa_decode_workspace_bytes sizes the workspace)
+ *   o, lse, max_seqlen, scale: as for fa_decode_varlen
+ *   workspace    at least fa_decode_split_workspace_bytes(B, H, d, max_seqlen,
+ *                split_keys or, for 0, fa_decode_paged_split_keys(...)) bytes,
+ *                with the counter rule of fa_decode_varlen
  *   page_size    tokens per page, a power of two, 1 .. 65536
  *   max_blocks   entries per block-table row; max_blocks * page_size >=
  *                max_seqlen, else FA_ERR_INVALID_ARG
- *   split_keys   as for fa_decode_varlen, and a chunk may span at most 1024
- *                pages (ceil(split_keys / page_size) + 1 <= 1024); 0 lets the
- *                library choose, as fa_decode_paged_split_keys reports (size
- *                the workspace with that value)
+ *   split_keys   as for fa_decode_varlen_split, and a chunk may span at most
+ *                1024 pages (ceil(split_keys / page_size) + 1 <= 1024); 0 lets
+ *                the library choose, as fa_decode_paged_split_keys reports
  *
  * fa_decode_paged_split_keys: the chunk size the library picks for split_keys
  * = 0 (the packed plan, halved while a chunk would span more than 1024
- * pages); 0 for invalid arguments.
+ * pages); 0 for invalid arguments or when no chunk size meets both the page
+ * limit and the 4096-chunk limit (fa_decode_paged then rejects split_keys =
+ * 0).  Every nonzero value it returns is accepted by fa_decode_paged.
  */
 int fa_decode_paged_split_keys(int B, int H, int d, int max_seqlen, int page_size);
 int fa_decode_paged(const void* q, const void* kpages, const void* vpages,

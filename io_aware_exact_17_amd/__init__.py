@@ -12,7 +12,13 @@ exception is raised.
     dq, dk, dv = fa_bwd(q, k, v, o, dout, lse, scale, causal)          # fp32 gradients
     o, lse = fa_fwd_block_sparse(q, k, v, block_mask, scale, causal)   # 64x64 block mask
     o, lse = fa_decode_varlen(q, kcache, vcache, seqlens, offsets, max_seqlen, scale)
+    o, lse = fa_decode_varlen_split(q, kcache, vcache, seqlens, offsets, max_seqlen, split_keys)
     o, lse = fa_decode_paged(q, kpages, vpages, block_table, seqlens, max_seqlen, scale)
+
+Every tensor the caller passes (inputs, and outputs or workspaces given in
+place of the ones the binding would allocate) is checked for dtype, shape,
+contiguity and device before the library is called: a wrong-sized buffer is
+refused here, never handed to a kernel.
 """
 from __future__ import annotations
 
@@ -41,8 +47,11 @@ SIGNATURES = {
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_split_keys": (_I, [_I, _I, _I, _I]),
-    "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
-    "fa_decode_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
+    "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "fa_decode_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _Z, _P]),
+    "fa_decode_split_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "fa_decode_varlen_split": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z,
+                                    _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_decode_paged_split_keys": (_I, [_I, _I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P,
@@ -100,43 +109,70 @@ def _stream(t, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _dev(t, name, dtype, ndim):
+def _dev(t, name, dtype, ndim, shape=None, device=None):
+    """Check a tensor handed to the library and return its device address.
+
+    shape: the exact shape required (None: any of `ndim` dims); device: the
+    device every tensor of the call must share (None: any HIP device)."""
     import torch
 
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's other tensors on {device}")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _extent(t, i, ndim):
+    """t.shape[i] when t is a tensor of ndim dims, else -1 (so that _dev then
+    reports what is wrong with t)."""
+    import torch
+
+    return t.shape[i] if isinstance(t, torch.Tensor) and t.dim() == ndim else -1
+
+
+def _workspace(ws, need, device, zero):
+    """A caller's workspace (uint8, >= need bytes, on `device`) or a new one;
+    decode workspaces are zero-filled (their arrival counters start at 0)."""
+    import torch
+
+    if ws is None:
+        alloc = torch.zeros if zero else torch.empty
+        ws = alloc(max(need, 16), dtype=torch.uint8, device=device)
+    _dev(ws, "workspace", torch.uint8, 1, device=device)
+    if ws.numel() < need:
+        raise ValueError(f"workspace has {ws.numel()} bytes, the call needs {need}")
+    return ws
 
 
 def _fwd(entry, dtype, q, k, v, scale, causal, out, lse, stream):
     import torch
 
     lib = load()
-    pq, pk, pv = _dev(q, "q", dtype, 4), _dev(k, "k", dtype, 4), _dev(v, "v", dtype, 4)
+    pq = _dev(q, "q", dtype, 4)
+    dev = q.device
     B, H, Nq, d = q.shape
-    if k.shape[:2] != (B, H) or k.shape[3] != d or v.shape != k.shape:
-        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    if not (q.device == k.device == v.device):
-        raise ValueError("q, k, v must be on one device")
-    Nk = k.shape[2]
+    Nk = _extent(k, 2, 4)
+    pk = _dev(k, "k", dtype, 4, (B, H, Nk, d), dev)
+    pv = _dev(v, "v", dtype, 4, (B, H, Nk, d), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    po = _dev(out, "out", dtype, 4)
-    pl = _dev(lse, "lse", torch.float32, 3)
-    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, Nq):
-        raise ValueError("out / lse shape mismatch")
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    po = _dev(out, "out", dtype, 4, q.shape, dev)
+    pl = _dev(lse, "lse", torch.float32, 3, (B, H, Nq), dev)
     with _on_device(q):
         st = getattr(lib, entry)(pq, pk, pv, po, pl, B, H, Nq, Nk, d, float(scale), int(bool(causal)),
                                  _stream(q, stream))
@@ -171,23 +207,20 @@ def fa_fwd_block_sparse(q, k, v, block_mask, scale=None, causal=False, out=None,
 
     lib = load()
     pq = _dev(q, "q", torch.bfloat16, 4)
-    pk = _dev(k, "k", torch.bfloat16, 4)
-    pv = _dev(v, "v", torch.bfloat16, 4)
-    pm = _dev(block_mask, "block_mask", torch.uint8, 3)
+    dev = q.device
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
-        raise ValueError("q, k, v shapes disagree")
-    if tuple(block_mask.shape) != (H, -(-Nq // 64), -(-Nk // 64)):
-        raise ValueError("block_mask must be [H, ceil(Nq/64), ceil(Nk/64)]")
+    Nk = _extent(k, 2, 4)
+    pk = _dev(k, "k", torch.bfloat16, 4, (B, H, Nk, d), dev)
+    pv = _dev(v, "v", torch.bfloat16, 4, (B, H, Nk, d), dev)
+    pm = _dev(block_mask, "block_mask", torch.uint8, 3, (H, -(-Nq // 64), -(-Nk // 64)), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    po = _dev(out, "out", torch.bfloat16, 4)
-    pl = _dev(lse, "lse", torch.float32, 3)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    po = _dev(out, "out", torch.bfloat16, 4, q.shape, dev)
+    pl = _dev(lse, "lse", torch.float32, 3, (B, H, Nq), dev)
     with _on_device(q):
         st = lib.fa_fwd_block_sparse(pq, pk, pv, po, pl, pm, B, H, Nq, Nk, d, float(scale),
                                      1 if causal else 0, _stream(q, stream))
@@ -206,25 +239,24 @@ def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv
     import torch
 
     lib = load()
-    ptrs = [_dev(t, n, torch.bfloat16, 4) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"),
-                                                       (dout, "dout"))]
-    pl = _dev(lse, "lse", torch.float32, 3)
+    pq = _dev(q, "q", torch.bfloat16, 4)
+    dev = q.device
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    if k.shape != (B, H, Nk, d) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
-        raise ValueError("q, k, v, o, dout shapes disagree")
-    if tuple(lse.shape) != (B, H, Nq):
-        raise ValueError("lse must be [B, H, Nq]")
+    Nk = _extent(k, 2, 4)
+    kshape = (B, H, Nk, d)
+    ptrs = [pq] + [_dev(t, n, torch.bfloat16, 4, shp, dev)
+                   for t, n, shp in ((k, "k", kshape), (v, "v", kshape), (o, "o", q.shape),
+                                     (dout, "dout", q.shape))]
+    pl = _dev(lse, "lse", torch.float32, 3, (B, H, Nq), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
-    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
-    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
-    gp = [_dev(t, n, torch.float32, 4) for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
-    if workspace is None:
-        workspace = torch.empty(max(fa_bwd_workspace_bytes(B, H, Nq), 16), dtype=torch.uint8,
-                                device=q.device)
-    pw = _dev(workspace, "workspace", torch.uint8, 1)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.empty(kshape, dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.empty(kshape, dtype=torch.float32, device=dev) if dv is None else dv
+    gp = [_dev(t, n, torch.float32, 4, shp, dev)
+          for t, n, shp in ((dq, "dq", q.shape), (dk, "dk", kshape), (dv, "dv", kshape))]
+    workspace = _workspace(workspace, fa_bwd_workspace_bytes(B, H, Nq), dev, zero=False)
+    pw = ctypes.c_void_p(workspace.data_ptr())
     with _on_device(q):
         st = lib.fa_bwd(*ptrs, pl, *gp, B, H, Nq, Nk, d, float(scale), 1 if causal else 0, pw,
                         workspace.numel(), _stream(q, stream))
@@ -241,24 +273,22 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None,
 
     lib = load()
     pq = _dev(q, "q", torch.bfloat16, 3)
-    pk = _dev(k, "k", torch.bfloat16, 3)
-    pv = _dev(v, "v", torch.bfloat16, 3)
-    pcq = _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
-    pck = _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    dev = q.device
     Tq, H, d = q.shape
-    if k.shape[1:] != (H, d) or v.shape != k.shape:
-        raise ValueError("q, k, v shapes disagree")
-    if cu_seqlens_k.shape != cu_seqlens_q.shape:
-        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B+1 entries")
+    Tk = _extent(k, 0, 3)
+    pk = _dev(k, "k", torch.bfloat16, 3, (Tk, H, d), dev)
+    pv = _dev(v, "v", torch.bfloat16, 3, (Tk, H, d), dev)
+    pcq = _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, device=dev)
     B = cu_seqlens_q.shape[0] - 1
+    pck = _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, (B + 1,), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
-    po = _dev(out, "out", torch.bfloat16, 3)
-    pl = _dev(lse, "lse", torch.float32, 2)
+        lse = torch.empty((H, Tq), dtype=torch.float32, device=dev)
+    po = _dev(out, "out", torch.bfloat16, 3, q.shape, dev)
+    pl = _dev(lse, "lse", torch.float32, 2, (H, Tq), dev)
     with _on_device(q):
         st = lib.fa_fwd_varlen(pq, pk, pv, po, pl, pcq, pck, B, H, d, Tq, int(max_seqlen_q),
                                float(scale), 1 if causal else 0, _stream(q, stream))
@@ -266,46 +296,76 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None,
     return out, lse
 
 
-def fa_decode_workspace_bytes(B, H, d, max_seqlen, split_keys=0) -> int:
-    return int(load().fa_decode_workspace_bytes(B, H, d, max_seqlen, split_keys))
+def fa_decode_workspace_bytes(B, H, d, max_seqlen) -> int:
+    return int(load().fa_decode_workspace_bytes(B, H, d, max_seqlen))
 
 
-def fa_decode_varlen(q, kcache, vcache, seqlens, offsets, max_seqlen, scale=None, split_keys=0,
-                     out=None, lse=None, workspace=None, stream=None):
-    """Decode over a packed cache: q [B,H,d], kcache/vcache [T,H,d] bf16,
-    seqlens/offsets int32 [B] on the device; max_seqlen a host int >= every
-    seqlens[b].  A caller-provided workspace is a uint8 tensor of at least
-    fa_decode_workspace_bytes bytes.  Returns (O bf16 [B,H,d], LSE fp32 [B,H])."""
+def fa_decode_split_workspace_bytes(B, H, d, max_seqlen, split_keys) -> int:
+    return int(load().fa_decode_split_workspace_bytes(B, H, d, max_seqlen, split_keys))
+
+
+def _decode_packed(split_keys, q, kcache, vcache, seqlens, offsets, max_seqlen, scale, out, lse,
+                   workspace, stream):
     import torch
 
     lib = load()
     pq = _dev(q, "q", torch.bfloat16, 3)
-    pk = _dev(kcache, "kcache", torch.bfloat16, 3)
-    pv = _dev(vcache, "vcache", torch.bfloat16, 3)
-    ps = _dev(seqlens, "seqlens", torch.int32, 1)
-    po_ = _dev(offsets, "offsets", torch.int32, 1)
+    dev = q.device
     B, H, d = q.shape
-    if kcache.shape[1:] != (H, d) or vcache.shape != kcache.shape:
-        raise ValueError("cache shape mismatch")
-    if seqlens.shape[0] != B or offsets.shape[0] != B:
-        raise ValueError("seqlens / offsets must have B entries")
+    T = _extent(kcache, 0, 3)
+    pk = _dev(kcache, "kcache", torch.bfloat16, 3, (T, H, d), dev)
+    pv = _dev(vcache, "vcache", torch.bfloat16, 3, (T, H, d), dev)
+    ps = _dev(seqlens, "seqlens", torch.int32, 1, (B,), dev)
+    po_ = _dev(offsets, "offsets", torch.int32, 1, (B,), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    po = _dev(out, "out", torch.bfloat16, 3)
-    pl = _dev(lse, "lse", torch.float32, 2)
-    need = fa_decode_workspace_bytes(B, H, d, int(max_seqlen), int(split_keys))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    pw = _dev(workspace, "workspace", torch.uint8, 1)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    po = _dev(out, "out", torch.bfloat16, 3, q.shape, dev)
+    pl = _dev(lse, "lse", torch.float32, 2, (B, H), dev)
+    if split_keys:
+        need = fa_decode_split_workspace_bytes(B, H, d, int(max_seqlen), int(split_keys))
+    else:
+        need = fa_decode_workspace_bytes(B, H, d, int(max_seqlen))
+    workspace = _workspace(workspace, need, dev, zero=True)
+    pw = ctypes.c_void_p(workspace.data_ptr())
     with _on_device(q):
-        st = lib.fa_decode_varlen(pq, pk, pv, ps, po_, po, pl, B, H, d, int(max_seqlen), float(scale),
-                                  int(split_keys), pw, workspace.numel(), _stream(q, stream))
-    _check(st, "fa_decode_varlen")
+        if split_keys:
+            entry = "fa_decode_varlen_split"
+            st = lib.fa_decode_varlen_split(pq, pk, pv, ps, po_, po, pl, B, H, d, int(max_seqlen),
+                                            float(scale), int(split_keys), pw, workspace.numel(),
+                                            _stream(q, stream))
+        else:
+            entry = "fa_decode_varlen"
+            st = lib.fa_decode_varlen(pq, pk, pv, ps, po_, po, pl, B, H, d, int(max_seqlen),
+                                      float(scale), pw, workspace.numel(), _stream(q, stream))
+    _check(st, entry)
     return out, lse
+
+
+def fa_decode_varlen(q, kcache, vcache, seqlens, offsets, max_seqlen, scale=None, out=None,
+                     lse=None, workspace=None, stream=None):
+    """Decode over a packed cache: q [B,H,d], kcache/vcache [T,H,d] bf16,
+    seqlens/offsets int32 [B] on the device; max_seqlen a host int >= every
+    seqlens[b].  A caller-provided workspace is a uint8 tensor of at least
+    fa_decode_workspace_bytes bytes whose first 64 KiB were zero-filled once
+    (torch.zeros); the library leaves them zero.  Without one, a zero-filled
+    workspace is allocated for the call.  Returns (O bf16 [B,H,d], LSE fp32
+    [B,H])."""
+    return _decode_packed(0, q, kcache, vcache, seqlens, offsets, max_seqlen, scale, out, lse,
+                          workspace, stream)
+
+
+def fa_decode_varlen_split(q, kcache, vcache, seqlens, offsets, max_seqlen, split_keys, scale=None,
+                           out=None, lse=None, workspace=None, stream=None):
+    """fa_decode_varlen with an explicit chunk size (a positive multiple of 64);
+    the workspace is sized by fa_decode_split_workspace_bytes."""
+    if int(split_keys) < 1:
+        raise ValueError("split_keys must be positive (fa_decode_varlen picks its own)")
+    return _decode_packed(int(split_keys), q, kcache, vcache, seqlens, offsets, max_seqlen, scale,
+                          out, lse, workspace, stream)
 
 
 def fa_decode_paged_split_keys(B, H, d, max_seqlen, page_size) -> int:
@@ -322,29 +382,26 @@ def fa_decode_paged(q, kpages, vpages, block_table, seqlens, max_seqlen, scale=N
 
     lib = load()
     pq = _dev(q, "q", torch.bfloat16, 3)
-    pk = _dev(kpages, "kpages", torch.bfloat16, 4)
-    pv = _dev(vpages, "vpages", torch.bfloat16, 4)
-    pb = _dev(block_table, "block_table", torch.int32, 2)
-    ps = _dev(seqlens, "seqlens", torch.int32, 1)
+    dev = q.device
     B, H, d = q.shape
-    num_pages, page_size = kpages.shape[0], kpages.shape[1]
-    if kpages.shape[2:] != (H, d) or vpages.shape != kpages.shape:
-        raise ValueError("page pool shape mismatch")
-    if block_table.shape[0] != B or seqlens.shape[0] != B:
-        raise ValueError("block_table / seqlens must have B rows")
+    num_pages, page_size = _extent(kpages, 0, 4), _extent(kpages, 1, 4)
+    pk = _dev(kpages, "kpages", torch.bfloat16, 4, (num_pages, page_size, H, d), dev)
+    pv = _dev(vpages, "vpages", torch.bfloat16, 4, (num_pages, page_size, H, d), dev)
+    max_blocks = _extent(block_table, 1, 2)
+    pb = _dev(block_table, "block_table", torch.int32, 2, (B, max_blocks), dev)
+    ps = _dev(seqlens, "seqlens", torch.int32, 1, (B,), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    po = _dev(out, "out", torch.bfloat16, 3)
-    pl = _dev(lse, "lse", torch.float32, 2)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    po = _dev(out, "out", torch.bfloat16, 3, q.shape, dev)
+    pl = _dev(lse, "lse", torch.float32, 2, (B, H), dev)
     sk = int(split_keys) or fa_decode_paged_split_keys(B, H, d, int(max_seqlen), int(page_size))
-    need = fa_decode_workspace_bytes(B, H, d, int(max_seqlen), sk)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    pw = _dev(workspace, "workspace", torch.uint8, 1)
+    need = fa_decode_split_workspace_bytes(B, H, d, int(max_seqlen), sk) if sk > 0 else 16
+    workspace = _workspace(workspace, need, dev, zero=True)
+    pw = ctypes.c_void_p(workspace.data_ptr())
     with _on_device(q):
         st = lib.fa_decode_paged(pq, pk, pv, pb, ps, po, pl, B, H, d, int(page_size), int(num_pages),
                                  int(block_table.shape[1]), int(max_seqlen), float(scale),

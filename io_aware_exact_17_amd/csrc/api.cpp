@@ -12,7 +12,15 @@ namespace {
 
 constexpr long long kMaxGridX = 0x7fffffffLL;  // HIP grid.x limit
 constexpr long long kMaxGridYZ = 65535;
-constexpr long long kMaxChunks = 256;  // chunks per sequence the merge kernel combines
+constexpr long long kPlanChunks = 256;    // chunks per sequence the automatic plan allows
+constexpr long long kMaxChunks = 4096;    // chunks per sequence the merge kernel combines
+constexpr long long kMaxFusedChunks = 1024;  // ... the last chunk to finish combines
+// Every decode workspace starts with this many arrival counters (4 bytes
+// each, 64 KiB), zero between calls; chunk states follow.  The region has a
+// fixed size so that no call's chunk states ever land on a counter, whatever
+// the shapes of earlier calls on the same workspace.
+constexpr long long kCounterSlots = 16384;
+constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
 constexpr long long kMaxPageSize = 1 << 16;   // tokens per page of a paged cache
 constexpr int kSparseBlock = 64;              // rows and keys per block-sparse mask block
 constexpr int kMaxSparseKeyBlocks = 1024;     // key blocks a block-sparse walk may list
@@ -53,21 +61,74 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
 int choose_split_keys(int B, int H, int max_seqlen) {
   long long sk = 256;
   while (sk < max_seqlen && ((long long)B * H * ((max_seqlen + sk - 1) / sk) > 16384 ||
-                             (max_seqlen + sk - 1) / sk > kMaxChunks))
+                             (max_seqlen + sk - 1) / sk > kPlanChunks))
     sk *= 2;
-  return (int)sk;
-}
-
-// The packed plan, halved while a chunk would span more pages than the
-// kernel stages in LDS.
-int choose_paged_split_keys(int B, int H, int max_seqlen, int page_size) {
-  long long sk = choose_split_keys(B, H, max_seqlen);
-  while ((sk + page_size - 1) / page_size + 1 > kMaxChunkPages && sk > 64) sk /= 2;
   return (int)sk;
 }
 
 bool page_size_ok(int page_size) {
   return page_size >= 1 && page_size <= kMaxPageSize && (page_size & (page_size - 1)) == 0;
+}
+
+// Chunk-size constraints every decode launch must meet: a positive multiple
+// of 64, at most kMaxChunks chunks per sequence and, for a paged cache, at
+// most kMaxChunkPages pages per chunk (a chunk that starts inside a page
+// spans one page more than its length needs).
+bool chunking_ok(long long max_seqlen, long long sk, int page_size) {
+  if (sk < 64 || sk % 64 != 0) return false;
+  if ((max_seqlen + sk - 1) / sk > kMaxChunks) return false;
+  if (page_size > 0 && (sk + page_size - 1) / page_size + 1 > kMaxChunkPages) return false;
+  return true;
+}
+
+// The packed plan, halved while a chunk would span more pages than the
+// kernel stages in LDS; 0 if no chunk size fits both limits.
+int choose_paged_split_keys(int B, int H, int max_seqlen, int page_size) {
+  long long sk = choose_split_keys(B, H, max_seqlen);
+  while ((sk + page_size - 1) / page_size + 1 > kMaxChunkPages && sk > 64) sk /= 2;
+  return chunking_ok(max_seqlen, sk, page_size) ? (int)sk : 0;
+}
+
+size_t split_workspace_bytes(int B, int H, int d, long long max_seqlen, long long sk) {
+  const long long n_splits = (max_seqlen + sk - 1) / sk;
+  // counters, then u[d] per (sequence, head, chunk), then (m, l) per chunk
+  return kCounterBytes + (size_t)B * (size_t)H * (size_t)n_splits * (size_t)(d + 2) * sizeof(float);
+}
+
+// Launch-time choice between the fused merge (last chunk to finish merges)
+// and the separate merge kernel: the fused one needs a counter per (sequence,
+// head) inside the fixed counter region.
+uint32_t* counters_for(void* workspace, int B, int H, long long n_splits) {
+  if ((long long)B * H > kCounterSlots || n_splits > kMaxFusedChunks) return nullptr;
+  return static_cast<uint32_t*>(workspace);
+}
+float* states_of(void* workspace) {
+  return reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+}
+
+int decode_packed(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens,
+                  const int32_t* offsets, void* o, float* lse, int B, int H, int d, int max_seqlen,
+                  float scale, int split_keys, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  if (!q || !kcache || !vcache || !seqlens || !offsets || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned4(o) ||
+      !aligned4(lse) || !aligned4(seqlens) || !aligned4(offsets))
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || max_seqlen < 1) return FA_ERR_INVALID_ARG;
+  if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_INVALID_ARG;  // grid.z / grid.x
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (split_keys < 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const int sk = split_keys > 0 ? split_keys : choose_split_keys(B, H, max_seqlen);
+  if (!chunking_ok(max_seqlen, sk, 0)) return FA_ERR_INVALID_ARG;
+  const long long n_splits = ((long long)max_seqlen + sk - 1) / sk;
+  const size_t need = split_workspace_bytes(B, H, d, max_seqlen, sk);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  fa::DecodeArgs a{q,  kcache, vcache, seqlens, offsets, nullptr,   0,  0,
+                   0,  o,      lse,    B,       H,       d,         max_seqlen, scale,
+                   sk, (int)n_splits, states_of(workspace), counters_for(workspace, B, H, n_splits),
+                   stream};
+  return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // namespace
@@ -163,36 +224,32 @@ int fa_decode_split_keys(int B, int H, int d, int max_seqlen) {
   return choose_split_keys(B, H, max_seqlen);
 }
 
-size_t fa_decode_workspace_bytes(int B, int H, int d, int max_seqlen, int split_keys) {
+size_t fa_decode_split_workspace_bytes(int B, int H, int d, int max_seqlen, int split_keys) {
   if (B < 1 || H < 1 || max_seqlen < 1 || (d != 64 && d != 128) || split_keys < 0) return 0;
   const long long sk = split_keys > 0 ? split_keys : choose_split_keys(B, H, max_seqlen);
-  const long long n_splits = (max_seqlen + sk - 1) / sk;
-  // chunk states: u[d] per (sequence, head, chunk), then (m, l) per chunk
-  return (size_t)B * (size_t)H * (size_t)n_splits * (size_t)(d + 2) * sizeof(float);
+  if (!chunking_ok(max_seqlen, sk, 0)) return 0;
+  return split_workspace_bytes(B, H, d, max_seqlen, sk);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int d, int max_seqlen) {
+  return fa_decode_split_workspace_bytes(B, H, d, max_seqlen, 0);
 }
 
 int fa_decode_varlen(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens,
                      const int32_t* offsets, void* o, float* lse, int B, int H, int d,
-                     int max_seqlen, float scale, int split_keys, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !kcache || !vcache || !seqlens || !offsets || !o || !lse) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned4(o) ||
-      !aligned4(lse) || !aligned4(seqlens) || !aligned4(offsets))
-    return FA_ERR_INVALID_ARG;
-  if (B < 1 || H < 1 || max_seqlen < 1) return FA_ERR_INVALID_ARG;
-  if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_INVALID_ARG;  // grid.z / grid.x
-  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
-  if (split_keys < 0 || split_keys % 64 != 0) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  const int sk = split_keys > 0 ? split_keys : choose_split_keys(B, H, max_seqlen);
-  const long long n_splits = ((long long)max_seqlen + sk - 1) / sk;
-  if (n_splits > kMaxChunks) return FA_ERR_INVALID_ARG;
-  const size_t need = fa_decode_workspace_bytes(B, H, d, max_seqlen, sk);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  fa::DecodeArgs a{q,  kcache, vcache, seqlens, offsets, nullptr,   0,  0,
-                   0,  o,      lse,    B,       H,       d,         max_seqlen, scale,
-                   sk, (int)n_splits, static_cast<float*>(workspace), stream};
-  return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+                     int max_seqlen, float scale, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  return decode_packed(q, kcache, vcache, seqlens, offsets, o, lse, B, H, d, max_seqlen, scale, 0,
+                       workspace, workspace_bytes, stream);
+}
+
+int fa_decode_varlen_split(const void* q, const void* kcache, const void* vcache,
+                           const int32_t* seqlens, const int32_t* offsets, void* o, float* lse,
+                           int B, int H, int d, int max_seqlen, float scale, int split_keys,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (split_keys < 1) return FA_ERR_INVALID_ARG;
+  return decode_packed(q, kcache, vcache, seqlens, offsets, o, lse, B, H, d, max_seqlen, scale,
+                       split_keys, workspace, workspace_bytes, stream);
 }
 
 int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
@@ -209,20 +266,19 @@ int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
   if (!page_size_ok(page_size)) return FA_ERR_INVALID_ARG;
   if ((long long)max_blocks * page_size < max_seqlen) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
-  if (split_keys < 0 || split_keys % 64 != 0) return FA_ERR_INVALID_ARG;
+  if (split_keys < 0) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   const long long sk = split_keys > 0 ? split_keys : choose_paged_split_keys(B, H, max_seqlen, page_size);
-  // a chunk that starts inside a page spans one page more than its length needs
-  if ((sk + page_size - 1) / page_size + 1 > kMaxChunkPages) return FA_ERR_INVALID_ARG;
+  if (!chunking_ok(max_seqlen, sk, page_size)) return FA_ERR_INVALID_ARG;
   const long long n_splits = ((long long)max_seqlen + sk - 1) / sk;
-  if (n_splits > kMaxChunks || n_splits > kMaxGridYZ) return FA_ERR_INVALID_ARG;
-  const size_t need = fa_decode_workspace_bytes(B, H, d, max_seqlen, (int)sk);
+  const size_t need = split_workspace_bytes(B, H, d, max_seqlen, sk);
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
   int shift = 0;
   while ((1 << shift) < page_size) ++shift;
   fa::DecodeArgs a{q,  kpages, vpages,     seqlens, nullptr, block_table, max_blocks, shift,
                    num_pages, o, lse,      B,       H,       d,           max_seqlen, scale,
-                   (int)sk, (int)n_splits, static_cast<float*>(workspace), stream};
+                   (int)sk, (int)n_splits, states_of(workspace),
+                   counters_for(workspace, B, H, n_splits), stream};
   return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -28,6 +28,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxChunkPages = 1024;  // pages one chunk may span (paged cache)
+constexpr int kMaxChunks = 4096;      // chunks per sequence the merge kernel combines
+constexpr int kMaxFusedChunks = 1024; // ... the last chunk to finish combines
 
 template <int D>
 struct DecCfg {
@@ -53,17 +55,113 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Device-coherent 8-byte store / load (relaxed, agent scope): they bypass
+// the per-XCD L2, so a workgroup on another XCD reads what the writer stored
+// once the writer's store has completed.
+__device__ __forceinline__ void store_coherent(float* p, float a, float b) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, f32x2{a, b}),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <bool COHERENT>
+__device__ __forceinline__ f32x2 load_state(const float* p) {
+  if constexpr (COHERENT)
+    return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p),
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  else
+    return *reinterpret_cast<const f32x2*>(p);
+}
+
+// Merge n >= 2 chunk states of one (sequence, head) with the block-merge
+// rule (explainer §3/§7) and write O = u / l (bf16) and LSE = m + ln l.
+// ml holds (m, l) per chunk (m in log2 units), u the unnormalised u[D] per
+// chunk.  Run by the first NW waves of the workgroup (threads 0 .. 64 NW - 1);
+// sm_cm / sm_cl hold one float per chunk; sm_red and sm_part are used when
+// NW > 1.  All (m, l) pairs are requested at once (64 NW per round), then the
+// waves split the chunks for the u sums (two dims per lane, eight loads in
+// flight), so the merge costs a few memory latencies, not one per chunk.
+template <int D, int NW, bool COHERENT>
+__device__ __forceinline__ void merge_chunks(const float* __restrict__ u, const float* __restrict__ ml,
+                                             int n, bf16* __restrict__ o_row,
+                                             float* __restrict__ lse_out, float* sm_cm, float* sm_cl,
+                                             float (*sm_red)[NW], float (*sm_part)[D]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float mloc = kNegInf;
+  for (int t = tid; t < n; t += 64 * NW) {
+    const f32x2 x = load_state<COHERENT>(ml + 2 * (size_t)t);
+    sm_cm[t] = x[0];
+    sm_cl[t] = x[1];
+    mloc = fmaxf(mloc, x[0]);
+  }
+  float M = wave_max(mloc);
+  if constexpr (NW > 1) {
+    if (lane == 0) sm_red[0][wave] = M;
+    __syncthreads();
+    M = sm_red[0][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_red[0][w]);
+  }
+  // Each thread turns its own chunks' m into the factor 2^(m - M).
+  float lloc = 0.f;
+  for (int t = tid; t < n; t += 64 * NW) {
+    const float f = exp2_hw(sm_cm[t] - M);
+    sm_cm[t] = f;
+    lloc = __builtin_fmaf(f, sm_cl[t], lloc);
+  }
+  float L = wave_sum(lloc);
+  if constexpr (NW > 1) {
+    if (lane == 0) sm_red[1][wave] = L;
+    __syncthreads();  // also orders the factors in sm_cm before the reads below
+    L = sm_red[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) L += sm_red[1][w];
+  }
+  const int d0 = 2 * lane;
+  float G0 = 0.f, G1 = 0.f;
+  if (d0 < D) {
+#pragma unroll 8
+    for (int t = wave; t < n; t += NW) {
+      const f32x2 w = load_state<COHERENT>(u + (size_t)t * D + d0);
+      G0 = __builtin_fmaf(sm_cm[t], w[0], G0);
+      G1 = __builtin_fmaf(sm_cm[t], w[1], G1);
+    }
+  }
+  if constexpr (NW > 1) {
+    if (d0 < D) {
+      sm_part[wave][d0] = G0;
+      sm_part[wave][d0 + 1] = G1;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    if (d0 < D) {
+      G0 = sm_part[0][d0];
+      G1 = sm_part[0][d0 + 1];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        G0 += sm_part[w][d0];
+        G1 += sm_part[w][d0 + 1];
+      }
+    }
+  }
+  const float inv = 1.f / L;
+  if (d0 < D) *reinterpret_cast<uint32_t*>(o_row + d0) = pack_bf16x2(G0 * inv, G1 * inv);
+  if (lane == 0) *lse_out = (M + log2_hw(L)) * kLn2;
+}
+
 // PAGED: the cache is a pool of pages [num_pages, page_size, H, d] and
 // sequence b's key t lives in page block_table[b][t / page_size], slot
 // t % page_size (page_size a power of two); otherwise the cache is packed
 // and sequence b owns rows offsets[b] ...
-template <int D, bool PAGED>
+//
+// FUSED: the chunks of a sequence that spans several are merged by the last
+// of them to finish, found through counters[b * H + h] (zero between calls).
+template <int D, bool PAGED, bool FUSED>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ seqlens, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ block_table, int bt_stride, int page_shift, int num_pages,
     bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ ws_u,
-    float* __restrict__ ws_ml, int H, int split_keys, int n_splits, float c) {
+    float* __restrict__ ws_ml, uint32_t* __restrict__ counters, int H, int split_keys,
+    int n_splits, float c) {
   using C = DecCfg<D>;
   // Heads vary fastest across the grid, so the workgroups running together
   // read neighbouring 256-byte head slices of the same token rows.
@@ -228,105 +326,87 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     return;
   }
 
-  // Leave this chunk's state for the merge kernel.
+  // Leave this chunk's state (u[D], then (m, l)) for the merge.
   const size_t slot = bh * n_splits + s;
-  if (has_d) *reinterpret_cast<f32x2*>(ws_u + slot * D + d0) = f32x2{U0, U1};
-  if (lane == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{M, L};
+  if constexpr (!FUSED) {
+    if (has_d) *reinterpret_cast<f32x2*>(ws_u + slot * D + d0) = f32x2{U0, U1};
+    if (lane == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{M, L};
+  } else {
+    if (has_d) store_coherent(ws_u + slot * D + d0, U0, U1);
+    if (lane == 0) store_coherent(ws_ml + slot * 2, M, L);
+    // The state has reached the coherence point before the arrival counts.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint32_t seen = 0;
+    if (lane == 0)
+      seen = __hip_atomic_fetch_add(counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    seen = __builtin_amdgcn_readfirstlane(seen);
+    if (seen != (uint32_t)(n_active - 1)) return;  // another chunk is still running
+    // Last to arrive: every other chunk's state is in place.  Reset the
+    // counter for the next call, then merge.
+    if (lane == 0) __hip_atomic_store(counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __shared__ float sm_cm[kMaxFusedChunks], sm_cl[kMaxFusedChunks];
+    merge_chunks<D, 1, true>(ws_u + bh * n_splits * D, ws_ml + bh * n_splits * 2, n_active, O + bh * D,
+                             LSE + bh, sm_cm, sm_cl, nullptr, nullptr);
+  }
 }
 
-// One 256-thread workgroup per (sequence, head) merges the chunk states.
-// Every chunk's (m, l) is requested at once, together with the sequence
-// length, and the four waves then split the chunks for the u sums, so the
-// merge costs a few memory latencies rather than one per chunk.  Sequences
-// that fitted in one chunk were finished by the split kernel.
+// One 256-thread workgroup per (sequence, head) merges the chunk states of
+// sequences that did not fit in one chunk (the others were finished by the
+// split kernel).
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(
     const float* __restrict__ ws_u, const float* __restrict__ ws_ml,
     const int32_t* __restrict__ seqlens, bf16* __restrict__ O, float* __restrict__ LSE, int H,
     int split_keys, int n_splits) {
+  constexpr int NW = kThreads / 64;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t bh = (size_t)b * H + h;
-  const size_t slot0 = bh * n_splits;
-  __shared__ float sm_f[kThreads];
-  __shared__ float sm_red[2][4];
-  __shared__ float sm_part[4][D];
-
+  __shared__ float sm_cm[kMaxChunks], sm_cl[kMaxChunks];
+  __shared__ float sm_red[2][NW];
+  __shared__ float sm_part[NW][D];
   const int len = seqlens[b];
-  // chunk states requested before the length is known (unused slots are
-  // never read as numbers: they are discarded by a select)
-  f32x2 ml = {kNegInf, 0.f};
-  if (tid < n_splits) ml = *reinterpret_cast<const f32x2*>(ws_ml + (slot0 + tid) * 2);
   const int n = min(n_splits, len > 0 ? (len + split_keys - 1) / split_keys : 0);
   if (n <= 1) return;  // empty or finished by the split kernel
-  const bool active = tid < n;
-  const float m_t = active ? ml[0] : kNegInf;
-  const float wmax = wave_max(m_t);
-  if (lane == 0) sm_red[0][wave] = wmax;
-  __syncthreads();
-  const float Mg = fmaxf(fmaxf(sm_red[0][0], sm_red[0][1]), fmaxf(sm_red[0][2], sm_red[0][3]));
-  const float f = active ? exp2_hw(m_t - Mg) : 0.f;
-  const float wl = wave_sum(active ? f * ml[1] : 0.f);
-  sm_f[tid] = f;
-  if (lane == 0) sm_red[1][wave] = wl;
-  __syncthreads();
-
-  // wave w sums chunks w, w+4, w+8, ... for dims 2*lane, 2*lane+1
-  const int d0 = 2 * lane;
-  float G0 = 0.f, G1 = 0.f;
-  if (d0 < D) {
-#pragma unroll 8
-    for (int t = wave; t < n; t += 4) {
-      const f32x2 w = *reinterpret_cast<const f32x2*>(ws_u + (slot0 + t) * D + d0);
-      G0 = __builtin_fmaf(sm_f[t], w[0], G0);
-      G1 = __builtin_fmaf(sm_f[t], w[1], G1);
-    }
-    sm_part[wave][d0] = G0;
-    sm_part[wave][d0 + 1] = G1;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const float Lg = sm_red[1][0] + sm_red[1][1] + sm_red[1][2] + sm_red[1][3];
-    const float inv = 1.f / Lg;
-    if (d0 < D) {
-      const float o0 = sm_part[0][d0] + sm_part[1][d0] + sm_part[2][d0] + sm_part[3][d0];
-      const float o1 = sm_part[0][d0 + 1] + sm_part[1][d0 + 1] + sm_part[2][d0 + 1] + sm_part[3][d0 + 1];
-      *reinterpret_cast<uint32_t*>(O + bh * D + d0) = pack_bf16x2(o0 * inv, o1 * inv);
-    }
-    if (lane == 0) LSE[bh] = (Mg + log2_hw(Lg)) * kLn2;
-  }
+  merge_chunks<D, NW, false>(ws_u + bh * n_splits * D, ws_ml + bh * n_splits * 2, n, O + bh * D,
+                             LSE + bh, sm_cm, sm_cl, sm_red, sm_part);
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool FUSED>
 hipError_t launch(const DecodeArgs& a) {
   const float c = a.scale * kLog2e;
   float* ws_u = a.ws;
   float* ws_ml = ws_u + (size_t)a.B * a.H * a.n_splits * D;
   {
-    void* args[] = {(void*)&a.q,          (void*)&a.kcache,    (void*)&a.vcache,
-                    (void*)&a.seqlens,    (void*)&a.offsets,   (void*)&a.block_table,
+    void* args[] = {(void*)&a.q,          (void*)&a.kcache,     (void*)&a.vcache,
+                    (void*)&a.seqlens,    (void*)&a.offsets,    (void*)&a.block_table,
                     (void*)&a.bt_stride,  (void*)&a.page_shift, (void*)&a.num_pages,
-                    (void*)&a.o,          (void*)&a.lse,       (void*)&ws_u,
-                    (void*)&ws_ml,        (void*)&a.H,         (void*)&a.split_keys,
-                    (void*)&a.n_splits,   (void*)&c};
+                    (void*)&a.o,          (void*)&a.lse,        (void*)&ws_u,
+                    (void*)&ws_ml,        (void*)&a.counters,   (void*)&a.H,
+                    (void*)&a.split_keys, (void*)&a.n_splits,   (void*)&c};
     const hipError_t e = hipLaunchKernel(
-        reinterpret_cast<const void*>(&decode_split_kernel<D, PAGED>),
+        reinterpret_cast<const void*>(&decode_split_kernel<D, PAGED, FUSED>),
         dim3((unsigned)a.H, (unsigned)a.n_splits, (unsigned)a.B), dim3(kThreads), args, 0, a.stream);
     if (e != hipSuccess) return e;
   }
-  if (a.n_splits == 1) return hipSuccess;  // every sequence finished in the split kernel
+  // every sequence finished in the split kernel (one chunk, or merged by its last chunk)
+  if (a.n_splits == 1 || FUSED) return hipSuccess;
   void* args[] = {(void*)&ws_u, (void*)&ws_ml, (void*)&a.seqlens, (void*)&a.o, (void*)&a.lse,
                   (void*)&a.H, (void*)&a.split_keys, (void*)&a.n_splits};
   return hipLaunchKernel(reinterpret_cast<const void*>(&decode_merge_kernel<D>),
                          dim3((unsigned)a.H, (unsigned)a.B), dim3(kThreads), args, 0, a.stream);
 }
 
+template <int D, bool PAGED>
+hipError_t launch_sel(const DecodeArgs& a) {
+  return a.counters ? launch<D, PAGED, true>(a) : launch<D, PAGED, false>(a);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a) {
   if (a.block_table)
-    return a.d == 128 ? launch<128, true>(a) : launch<64, true>(a);
-  return a.d == 128 ? launch<128, false>(a) : launch<64, false>(a);
+    return a.d == 128 ? launch_sel<128, true>(a) : launch_sel<64, true>(a);
+  return a.d == 128 ? launch_sel<128, false>(a) : launch_sel<64, false>(a);
 }
 
 }  // namespace fa

@@ -47,7 +47,10 @@ struct DecodeArgs {
   float scale;
   int split_keys;  // resolved (> 0)
   int n_splits;    // ceil(max_seqlen / split_keys)
-  float* ws;       // workspace, decode_workspace_floats(...) floats
+  float* ws;       // chunk states: u [B, H, n_splits, d], then (m, l) [B, H, n_splits, 2]
+  // Arrival counters [B * H], zero between calls: the last chunk of a
+  // sequence to finish merges (no merge kernel).  Null: a merge kernel runs.
+  uint32_t* counters;
   hipStream_t stream;
 };
 

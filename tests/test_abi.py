@@ -102,42 +102,82 @@ def test_varlen_rejects_bad_arguments():
 
 
 def dec_call(q=A, kc=A, vc=A, sl=A2, off=A2, o=A2, lse=A2, B=2, H=4, d=128, max_seqlen=100,
-             scale=0.1, split_keys=0, ws=A, ws_bytes=1 << 30):
+             scale=0.1, ws=A, ws_bytes=1 << 30):
+    """fa_decode_varlen with exactly the parameters of the boundary's signature."""
     lib = fa.load()
-    return lib.fa_decode_varlen(q, kc, vc, sl, off, o, lse, B, H, d, max_seqlen, scale,
-                                split_keys, ws, ws_bytes, None)
+    return lib.fa_decode_varlen(q, kc, vc, sl, off, o, lse, B, H, d, max_seqlen, scale, ws,
+                                ws_bytes, None)
+
+
+def dec_split_call(split_keys=64, **kw):
+    lib = fa.load()
+    a = dict(q=A, kc=A, vc=A, sl=A2, off=A2, o=A2, lse=A2, B=2, H=4, d=128, max_seqlen=100,
+             scale=0.1, ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.fa_decode_varlen_split(a["q"], a["kc"], a["vc"], a["sl"], a["off"], a["o"], a["lse"],
+                                      a["B"], a["H"], a["d"], a["max_seqlen"], a["scale"], split_keys,
+                                      a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_signature_is_the_boundary():
+    """fa_decode_varlen / fa_decode_workspace_bytes take exactly the boundary's
+    parameters (q, kcache, vcache, seqlens, offsets, o, lse, B, H, d,
+    max_seqlen, scale, workspace, workspace_bytes, stream)."""
+    header = open(os.path.join(ROOT, "include", "fa.h")).read()
+    flat = re.sub(r"\s+", " ", header)
+    assert ("int fa_decode_varlen(const void* q, const void* kcache, const void* vcache, "
+            "const int32_t* seqlens, const int32_t* offsets, void* o, float* lse, int B, int H, "
+            "int d, int max_seqlen, float scale, void* workspace, size_t workspace_bytes, "
+            "hipStream_t stream);") in flat
+    assert "size_t fa_decode_workspace_bytes(int B, int H, int d, int max_seqlen);" in flat
+    assert len(fa.SIGNATURES["fa_decode_varlen"][1]) == 15
+    assert len(fa.SIGNATURES["fa_decode_workspace_bytes"][1]) == 4
 
 
 def test_decode_rejects_invalid_arguments():
     for kw in ("q", "kc", "vc", "sl", "off", "o", "lse"):
         assert dec_call(**{kw: None}) == INVALID
+        assert dec_split_call(**{kw: None}) == INVALID
     assert dec_call(kc=A + 4) == INVALID
     assert dec_call(sl=A2 + 1) == INVALID
     for bad in ({"B": 0}, {"H": 0}, {"max_seqlen": 0}, {"B": 70000}, {"H": 70000}):
         assert dec_call(**bad) == INVALID
+        assert dec_split_call(**bad) == INVALID
     assert dec_call(scale=float("nan")) == INVALID
-    assert dec_call(split_keys=-64) == INVALID
-    assert dec_call(split_keys=100) == INVALID  # not a multiple of 64
-    assert dec_call(split_keys=64, max_seqlen=64 * 257, ws_bytes=1 << 40) == INVALID  # > 256 chunks
+    assert dec_split_call(split_keys=0) == INVALID     # the split entry needs an explicit size
+    assert dec_split_call(split_keys=-64) == INVALID
+    assert dec_split_call(split_keys=100) == INVALID   # not a multiple of 64
+    assert dec_split_call(split_keys=64, max_seqlen=64 * 4097, ws_bytes=1 << 40) == INVALID  # > 4096 chunks
     assert dec_call(d=96) == UNSUPPORTED
+    assert dec_split_call(d=96) == UNSUPPORTED
     assert dec_call(ws=None) == WORKSPACE
     assert dec_call(ws=A + 8) == WORKSPACE
-    need = fa.fa_decode_workspace_bytes(2, 4, 128, 100, 0)
+    need = fa.fa_decode_workspace_bytes(2, 4, 128, 100)
     assert dec_call(ws_bytes=need - 1) == WORKSPACE
+    need64 = fa.fa_decode_split_workspace_bytes(2, 4, 128, 100, 64)
+    assert dec_split_call(ws_bytes=need64 - 1) == WORKSPACE
+
+
+COUNTER_BYTES = 65536  # arrival counters at the start of every decode workspace
 
 
 def test_workspace_and_split_plan():
     # a single long sequence is cut into 256-key chunks
     assert fa.fa_decode_split_keys(1, 32, 128, 8192) == 256
-    assert fa.fa_decode_workspace_bytes(1, 32, 128, 8192, 0) == 1 * 32 * 32 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(1, 32, 128, 8192) == COUNTER_BYTES + 1 * 32 * 32 * 130 * 4
+    assert fa.fa_decode_split_workspace_bytes(1, 32, 128, 8192, 0) == fa.fa_decode_workspace_bytes(
+        1, 32, 128, 8192)
     # a large batch gets longer chunks, keeping the grid <= 16384 workgroups
     sk = fa.fa_decode_split_keys(64, 32, 128, 16384)
     assert sk == 2048 and 64 * 32 * -(-16384 // sk) <= 16384
-    assert fa.fa_decode_workspace_bytes(3, 5, 64, 1000, 128) == 3 * 5 * 8 * 66 * 4
-    # at most 256 chunks per sequence
+    assert fa.fa_decode_split_workspace_bytes(3, 5, 64, 1000, 128) == COUNTER_BYTES + 3 * 5 * 8 * 66 * 4
+    # the automatic plan keeps at most 256 chunks per sequence
     assert -(-(1 << 24) // fa.fa_decode_split_keys(1, 1, 128, 1 << 24)) <= 256
-    assert fa.fa_decode_workspace_bytes(0, 5, 64, 1000, 128) == 0
-    assert fa.fa_decode_workspace_bytes(3, 5, 96, 1000, 128) == 0
+    assert fa.fa_decode_split_workspace_bytes(0, 5, 64, 1000, 128) == 0
+    assert fa.fa_decode_split_workspace_bytes(3, 5, 96, 1000, 128) == 0
+    assert fa.fa_decode_split_workspace_bytes(3, 5, 64, 1000, 100) == 0      # not a multiple of 64
+    assert fa.fa_decode_split_workspace_bytes(1, 1, 64, 64 * 4097, 64) == 0  # > 4096 chunks
+    assert fa.fa_decode_workspace_bytes(0, 5, 64, 1000) == 0
 
 
 @pytest.mark.skipif(gpu_available(), reason="uses fake device pointers; only safe with no GPU")
@@ -147,6 +187,7 @@ def test_valid_call_without_gpu_reports_hip_error():
     assert fwd_call() == HIPERR
     assert fwd_call("fa_fwd_f32", d=128, causal=1) == HIPERR
     assert dec_call() == HIPERR
+    assert dec_split_call(split_keys=128) == HIPERR
 
 
 def test_binding_validates_tensors():
@@ -188,7 +229,8 @@ def test_decode_paged_rejects_invalid_arguments():
     assert paged_call(split_keys=96) == INVALID
     assert paged_call(d=96) == UNSUPPORTED
     assert paged_call(ws=None) == WORKSPACE
-    need = fa.fa_decode_workspace_bytes(2, 4, 128, 100, fa.fa_decode_paged_split_keys(2, 4, 128, 100, 16))
+    need = fa.fa_decode_split_workspace_bytes(2, 4, 128, 100,
+                                              fa.fa_decode_paged_split_keys(2, 4, 128, 100, 16))
     assert paged_call(ws_bytes=need - 1) == WORKSPACE
 
 
@@ -198,6 +240,27 @@ def test_decode_paged_split_plan():
     sk = fa.fa_decode_paged_split_keys(1, 1, 128, 1 << 20, 1)
     assert sk % 64 == 0 and sk + 1 <= 1024
     assert fa.fa_decode_paged_split_keys(1, 1, 128, 100, 3) == 0
+    # no chunk size meets both the 1024-page and the 4096-chunk limits
+    assert fa.fa_decode_paged_split_keys(1, 1, 128, 1 << 23, 1) == 0
+    assert paged_call(page=1, max_blocks=1 << 23, max_seqlen=1 << 23) == INVALID
+
+
+@pytest.mark.skipif(gpu_available(), reason="uses fake device pointers; only safe with no GPU")
+@pytest.mark.parametrize("B,H,max_seqlen,page", [
+    (1, 32, 8192, 16), (64, 32, 16384, 16), (1, 1, 200000, 1), (1, 8, 1 << 22, 2),
+    (3, 5, 1000, 1024), (2, 2, (1 << 23) - 1, 4), (1, 1, 1, 1), (1, 1, 65536 * 8, 65536)])
+def test_every_paged_plan_is_accepted(B, H, max_seqlen, page):
+    """Whatever nonzero chunk size fa_decode_paged_split_keys reports, fa_decode_paged
+    accepts: its checks pass and the call reaches the (absent) HIP runtime."""
+    sk = fa.fa_decode_paged_split_keys(B, H, 128, max_seqlen, page)
+    if sk == 0:
+        return
+    need = fa.fa_decode_split_workspace_bytes(B, H, 128, max_seqlen, sk)
+    assert need > 0
+    mb = -(-max_seqlen // page)
+    for split in (0, sk):
+        assert paged_call(B=B, H=H, page=page, max_blocks=mb, max_seqlen=max_seqlen,
+                          split_keys=split, ws_bytes=need) == HIPERR
 
 
 

@@ -88,6 +88,25 @@ def test_prefill_full_size_sampled(fa, spec):
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
+def test_long_prefill_whole_output(fa):
+    """The long causal prefill (B=1, H=32, N=8192, d=128) in the launch the
+    benchmark times: every element of O and LSE of all 32 heads against the
+    oracle, head by head."""
+    s = W.LONG_PREFILL
+    log(f"case {s.name} whole output")
+    q, k, v = W.prefill_spec_inputs(s, "cuda")
+    o, lse = run_fwd(fa, q, k, v, s.scale, s.causal)
+    oh, lh = o.cpu(), lse.cpu()
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    worst_o = worst_l = 0.0
+    for h in range(s.H):
+        O, L = oracle.head_attention(qh[0, h], kh[0, h], vh[0, h], s.scale, s.causal)
+        worst_o = max(worst_o, max_err(W.to_f64(oh[0, h]), O))
+        worst_l = max(worst_l, max_err(W.to_f64(lh[0, h]), L))
+    log(f"  all {s.H} heads: err_O={worst_o:.3e} err_LSE={worst_l:.3e}")
+    assert worst_o <= TOL_BF16 and worst_l <= TOL_LSE
+
+
 def test_prefill_gpt2m_whole_heads(fa):
     """Complete heads of the GPT-2-medium shape, every row, causal and not."""
     for spec in (W.GPT2M, W.GPT2M_CAUSAL):
@@ -156,17 +175,72 @@ def test_large_scores(fa, d):
         check(o, lse, O, L, TOL_BF16, f"large scores d={d} causal={causal}")
 
 
-def test_deterministic(fa):
-    log("case determinism")
-    q, k, v = W.prefill_inputs(2, 4, 520, 520, 128, "bf16", seed=9, device="cuda")
-    o1, l1 = run_fwd(fa, q, k, v, 0.088, True)
-    o2, l2 = run_fwd(fa, q, k, v, 0.088, True)
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+@pytest.mark.parametrize("d,B,H,N", [(128, 2, 4, 520), (64, 3, 200, 600)])
+def test_deterministic(fa, d, B, H, N):
+    """Run-to-run bit-identical prefill (d = 64: a stream with more query tiles
+    than CUs)."""
+    log(f"case determinism d={d}")
+    q, k, v = W.prefill_inputs(B, H, N, N, d, "bf16", seed=9, device="cuda")
+    for causal in (True, False):
+        o1, l1 = run_fwd(fa, q, k, v, 0.088, causal)
+        o2, l2 = run_fwd(fa, q, k, v, 0.088, causal)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), causal
+
+
+def test_binding_refuses_wrong_buffers(fa):
+    """Caller-supplied outputs, gradients and workspaces of the wrong shape,
+    dtype or device are refused by the binding before anything is launched."""
+    log("case binding validation")
+    dev = "cuda"
+    q, k, v = W.prefill_inputs(1, 2, 64, 80, 128, "bf16", seed=3, device=dev)
+    bad_out = torch.empty(1, 2, 63, 128, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, k, v, out=bad_out)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, k, v, lse=torch.empty(1, 2, 65, device=dev))
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, k.cpu(), v)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, k[:, :, :40].contiguous(), v)  # k and v lengths differ
+    o, lse = fa.fa_fwd(q, k, v)
+    do = torch.randn_like(q)
+    for kw in ({"dq": torch.empty(1, 2, 64, 127, device=dev)},
+               {"dk": torch.empty(1, 2, 64, 128, device=dev)},
+               {"dv": torch.empty(1, 2, 80, 128, dtype=torch.bfloat16, device=dev)},
+               {"workspace": torch.empty(8, dtype=torch.uint8, device=dev)}):
+        with pytest.raises(ValueError):
+            fa.fa_bwd(q, k, v, o, do, lse, **kw)
+    m = W.block_mask("ones", 2, 64, 80).to(dev)
+    with pytest.raises(ValueError):
+        fa.fa_fwd_block_sparse(q, k, v, m, out=bad_out)
+    lens = [5, 9]
+    dq_, dkc, dvc, sl, off = W.decode_inputs(2, 2, 128, lens, seed=1, device=dev)
+    with pytest.raises(ValueError):
+        fa.fa_decode_varlen(dq_, dkc, dvc, sl, off, 9, out=torch.empty(2, 2, 64, dtype=torch.bfloat16,
+                                                                        device=dev))
+    with pytest.raises(ValueError):
+        fa.fa_decode_varlen(dq_, dkc, dvc, sl, off, 9, lse=torch.empty(2, 3, device=dev))
+    with pytest.raises(ValueError):
+        fa.fa_decode_varlen(dq_, dkc, dvc, sl, off, 9,
+                            workspace=torch.zeros(16, dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError):
+        fa.fa_decode_varlen(dq_, dkc, dvc, sl[:1].contiguous(), off, 9)
+    lq = [30, 10]
+    vq, vk, vv, cq, ck = W.varlen_inputs(lq, lq, 2, 128, seed=2, device=dev)
+    with pytest.raises(ValueError):
+        fa.fa_fwd_varlen(vq, vk, vv, cq, ck, 30, lse=torch.empty(2, 39, device=dev))
+    with pytest.raises(ValueError):
+        fa.fa_fwd_varlen(vq, vk, vv, cq, ck[:2].contiguous(), 30)
+    torch.cuda.synchronize()
 
 
 # ------------------------------------------------------------- decode
-def run_decode(fa, q, kc, vc, sl, off, max_len, scale, split_keys=0):
-    o, lse = fa.fa_decode_varlen(q, kc, vc, sl, off, max_len, scale, split_keys)
+def run_decode(fa, q, kc, vc, sl, off, max_len, scale, split_keys=0, workspace=None):
+    if split_keys:
+        o, lse = fa.fa_decode_varlen_split(q, kc, vc, sl, off, max_len, split_keys, scale,
+                                           workspace=workspace)
+    else:
+        o, lse = fa.fa_decode_varlen(q, kc, vc, sl, off, max_len, scale, workspace=workspace)
     torch.cuda.synchronize()
     return o, lse
 
@@ -180,17 +254,23 @@ def test_decode_single_full(fa):
     check(o, lse, O, L, TOL_BF16, s.name)
 
 
-def test_decode_batched_full_size_sampled(fa):
+def test_decode_batched_full_size(fa):
+    """The batched decode workload in the benchmark's launch: all 64 sequences
+    against the oracle on three heads (first, a middle one, last), and the
+    whole output twice over for run-to-run equality."""
     s = W.DECODE_BATCHED
     log(f"case {s.name}")
     q, kc, vc, sl, off = W.decode_spec_inputs(s, "cuda")
     log(f"  T={kc.shape[0]} tokens, {kc.numel() * 4 / 1e9:.2f} GB of K+V")
     o, lse = run_decode(fa, q, kc, vc, sl, off, s.max_len, s.scale)
     slh, offh = sl.cpu(), off.cpu()
-    seqs = sorted({0, s.B - 1, int(torch.argmax(slh)), int(torch.argmin(slh)), 7, 31})
-    O, L = oracle.decode(q, kc, vc, slh, offh, s.scale, seqs=seqs)
-    check(o[seqs], lse[seqs], O[seqs], L[seqs], TOL_BF16, s.name + " sampled sequences")
+    heads = [0, 13, s.H - 1]
+    O, L = oracle.decode(q, kc, vc, slh, offh, s.scale, heads=heads)
+    check(o[:, heads], lse[:, heads], O[:, heads], L[:, heads], TOL_BF16,
+          s.name + " all sequences, heads 0/13/31")
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    o2, lse2 = run_decode(fa, q, kc, vc, sl, off, s.max_len, s.scale)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "batched decode not deterministic"
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -234,19 +314,59 @@ def test_decode_matches_fwd_single_query(fa):
         assert (of[0, :, 0].float() - o[b].float()).abs().max().item() <= 2e-2
 
 
+COUNTER_BYTES = 65536  # arrival counters at the start of every decode workspace
+
+
 def test_decode_workspace_reused_across_calls(fa):
-    """One workspace serves consecutive calls with different inputs."""
+    """One zero-filled workspace serves consecutive calls of different shapes
+    and chunk sizes (the chunk states of one call land where another call's
+    would not); the arrival counters are zero again after every call."""
     log("case decode workspace reuse")
-    lens = [700, 64, 3000, 1]
-    B, H, d = len(lens), 4, 128
-    ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, d, max(lens), 256), dtype=torch.uint8,
-                     device="cuda")
-    for call in range(3):
-        q, kc, vc, sl, off = W.decode_inputs(B, H, d, lens, seed=100 + call, device="cuda")
-        o, lse = fa.fa_decode_varlen(q, kc, vc, sl, off, max(lens), 0.088, 256, workspace=ws)
-        torch.cuda.synchronize()
+    cases = [([700, 64, 3000, 1], 4, 256), ([5000] * 9, 7, 64), ([700, 64, 3000, 1], 4, 0),
+             ([1, 2, 3], 40, 64), ([8192], 32, 0)]
+    need = max(fa.fa_decode_split_workspace_bytes(len(l), H, 128, max(l), sk or 256)
+               for l, H, sk in cases)
+    need = max(need, max(fa.fa_decode_workspace_bytes(len(l), H, 128, max(l)) for l, H, _ in cases))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for call, (lens, H, sk) in enumerate(cases):
+        q, kc, vc, sl, off = W.decode_inputs(len(lens), H, 128, lens, seed=100 + call, device="cuda")
+        o, lse = run_decode(fa, q, kc, vc, sl, off, max(lens), 0.088, sk, workspace=ws)
         O, L = oracle.decode(q, kc, vc, sl.cpu(), off.cpu(), 0.088)
-        check(o, lse, O, L, TOL_BF16, f"reuse call {call}")
+        check(o, lse, O, L, TOL_BF16, f"reuse call {call} B={len(lens)} H={H} split_keys={sk}")
+        assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0, "arrival counters left nonzero"
+
+
+def test_decode_merge_paths_agree(fa):
+    """The merge by the last chunk to finish (counters) and the separate merge
+    kernel (beyond 1024 chunks per sequence, or more than 16384 sequence-head
+    pairs) against the oracle, and against each other within fp32 rounding."""
+    log("case decode merge paths")
+    lens = [64 * 1100, 3000, 1]
+    q, kc, vc, sl, off = W.decode_inputs(len(lens), 2, 128, lens, seed=41, device="cuda")
+    O, L = oracle.decode(q, kc, vc, sl.cpu(), off.cpu(), 0.088)
+    o1, l1 = run_decode(fa, q, kc, vc, sl, off, max(lens), 0.088, 64)     # 1100 chunks: kernel
+    o2, l2 = run_decode(fa, q, kc, vc, sl, off, max(lens), 0.088, 128)    # 550 chunks: fused
+    check(o1, l1, O, L, TOL_BF16, "merge kernel")
+    check(o2, l2, O, L, TOL_BF16, "fused merge")
+    # many (sequence, head) pairs: 4100 x 4 > 16384 counters -> merge kernel
+    lens2 = [(i * 37) % 900 for i in range(4100)]
+    q, kc, vc, sl, off = W.decode_inputs(len(lens2), 4, 64, lens2, seed=43, device="cuda")
+    o3, l3 = run_decode(fa, q, kc, vc, sl, off, max(lens2), 0.125, 256)
+    seqs = [0, 1, 25, 1000, 4099]
+    O3, L3 = oracle.decode(q, kc, vc, sl.cpu(), off.cpu(), 0.125, seqs=seqs)
+    check(o3[seqs], l3[seqs], O3[seqs], L3[seqs], TOL_BF16, "16400 sequence-head pairs")
+
+
+def test_decode_deterministic(fa):
+    """Decode is run-to-run bit-identical: single request (fused merge) and an
+    explicit chunking that takes the merge kernel."""
+    log("case decode determinism")
+    s = W.DECODE_SINGLE
+    q, kc, vc, sl, off = W.decode_spec_inputs(s, "cuda")
+    for sk in (0, 64):
+        a = run_decode(fa, q, kc, vc, sl, off, s.max_len, s.scale, sk)
+        b = run_decode(fa, q, kc, vc, sl, off, s.max_len, s.scale, sk)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), sk
 
 
 VARLEN_CASES = [
@@ -456,7 +576,7 @@ def test_decode_paged(fa, d, P, sk):
     bt, kp, vp = paged_copy(kc, vc, sl, off, P, seed=P)
     o, lse = fa.fa_decode_paged(q, kp, vp, bt.to("cuda"), sl, max(lens), 0.088, sk)
     sk_used = sk or fa.fa_decode_paged_split_keys(B, H, d, max(lens), P)
-    o2, lse2 = fa.fa_decode_varlen(q, kc, vc, sl, off, max(lens), 0.088, sk_used)
+    o2, lse2 = fa.fa_decode_varlen_split(q, kc, vc, sl, off, max(lens), sk_used, 0.088)
     torch.cuda.synchronize()
     O, L = oracle.decode_paged(q, kp, vp, bt, sl.cpu(), 0.088)
     check(o, lse, O, L, TOL_BF16, f"paged page={P}")
@@ -484,7 +604,7 @@ def test_decode_paged_batched_full_size(fa):
     del kp, vp
     q2, kc, vc, sl2, off2 = W.decode_spec_inputs(s, "cuda")
     sk = fa.fa_decode_paged_split_keys(s.B, s.H, s.d, s.max_len, 16)
-    o2, lse2 = fa.fa_decode_varlen(q2, kc, vc, sl2, off2, s.max_len, s.scale, sk)
+    o2, lse2 = fa.fa_decode_varlen_split(q2, kc, vc, sl2, off2, s.max_len, sk, s.scale)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
