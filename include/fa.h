@@ -62,7 +62,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, non-finite scale, size too large */
   FA_ERR_UNSUPPORTED = -2, /* head dimension other than 64 or 128 */
   FA_ERR_WORKSPACE = -3,   /* decode workspace missing or smaller than required */
-  FA_ERR_HIP = -4          /* the HIP runtime refused the launch */
+  FA_ERR_HIP = -4,         /* the HIP runtime refused the launch */
+  FA_ERR_SCRATCH = -5      /* more chunk state than fa_decode_varlen_noalloc's fixed scratch */
 } fa_status;
 
 /*
@@ -274,6 +275,32 @@ int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
                     int max_seqlen, float scale, int split_keys,
                     void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/*
+ * fa_decode_varlen without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same computation, arguments and results as
+ * fa_decode_varlen with the automatic chunk size, minus the workspace: the
+ * chunk states go to a fixed scratch array of FA_DECODE_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that the library holds on each device it runs on until the
+ * process ends, and a second kernel merges them.  The call allocates and
+ * frees nothing.
+ *
+ * Limit: B * H * ceil(max_seqlen / fa_decode_split_keys(B, H, d, max_seqlen))
+ * * (d + 2) * 4 bytes must not exceed the scratch (e.g. 64 sequences x 32
+ * heads of up to 16384 keys at d = 128 use 8.5 MB); larger calls return
+ * FA_ERR_SCRATCH before any HIP call.  Nothing in the scratch needs to start
+ * at zero.  All calls on one device share its scratch: calls that overlap in
+ * time on one device (other streams, other threads) race and give wrong
+ * results; calls ordered on one stream are safe.  The first call on a device
+ * looks up that device's scratch address (a runtime query, no allocation).
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_decode_varlen_noalloc(const void* q, const void* kcache, const void* vcache,
+                             const int32_t* seqlens, const int32_t* offsets,
+                             void* o, float* lse,
+                             int B, int H, int d, int max_seqlen, float scale,
+                             hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_string(int status);

@@ -33,6 +33,7 @@ FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_WORKSPACE = -3
 FA_ERR_HIP = -4
+FA_ERR_SCRATCH = -5
 
 # Every symbol the C ABI exports, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -57,6 +58,7 @@ SIGNATURES = {
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P,
                              _Z, _P]),
     "fa_probe_read": (_I, [_P, _Z, _P, _P]),
+    "fa_decode_varlen_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
 }
 
 _lib = None
@@ -366,6 +368,38 @@ def fa_decode_varlen_split(q, kcache, vcache, seqlens, offsets, max_seqlen, spli
         raise ValueError("split_keys must be positive (fa_decode_varlen picks its own)")
     return _decode_packed(int(split_keys), q, kcache, vcache, seqlens, offsets, max_seqlen, scale,
                           out, lse, workspace, stream)
+
+
+def fa_decode_varlen_noalloc(q, kcache, vcache, seqlens, offsets, max_seqlen, scale=None, out=None,
+                             lse=None, stream=None):
+    """fa_decode_varlen without a workspace: the library's fixed per-device
+    scratch holds the chunk states (include/fa.h states the size limit and
+    that calls overlapping on one device race).  The C call allocates
+    nothing; pass `out` and `lse` to keep this wrapper from allocating them."""
+    import torch
+
+    lib = load()
+    pq = _dev(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    B, H, d = q.shape
+    T = _extent(kcache, 0, 3)
+    pk = _dev(kcache, "kcache", torch.bfloat16, 3, (T, H, d), dev)
+    pv = _dev(vcache, "vcache", torch.bfloat16, 3, (T, H, d), dev)
+    ps = _dev(seqlens, "seqlens", torch.int32, 1, (B,), dev)
+    po_ = _dev(offsets, "offsets", torch.int32, 1, (B,), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    po = _dev(out, "out", torch.bfloat16, 3, q.shape, dev)
+    pl = _dev(lse, "lse", torch.float32, 2, (B, H), dev)
+    with _on_device(q):
+        st = lib.fa_decode_varlen_noalloc(pq, pk, pv, ps, po_, po, pl, B, H, d, int(max_seqlen),
+                                          float(scale), _stream(q, stream))
+    _check(st, "fa_decode_varlen_noalloc")
+    return out, lse
 
 
 def fa_decode_paged_split_keys(B, H, d, max_seqlen, page_size) -> int:

@@ -282,6 +282,31 @@ int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
   return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_decode_varlen_noalloc(const void* q, const void* kcache, const void* vcache,
+                             const int32_t* seqlens, const int32_t* offsets, void* o, float* lse,
+                             int B, int H, int d, int max_seqlen, float scale, hipStream_t stream) {
+  if (!q || !kcache || !vcache || !seqlens || !offsets || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned4(o) ||
+      !aligned4(lse) || !aligned4(seqlens) || !aligned4(offsets))
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || max_seqlen < 1) return FA_ERR_INVALID_ARG;
+  if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const int sk = choose_split_keys(B, H, max_seqlen);
+  if (!chunking_ok(max_seqlen, sk, 0)) return FA_ERR_INVALID_ARG;
+  const long long n_splits = ((long long)max_seqlen + sk - 1) / sk;
+  // chunk states only: this path merges with the merge kernel, no counters
+  const size_t need = (size_t)B * (size_t)H * (size_t)n_splits * (size_t)(d + 2) * sizeof(float);
+  if (need > (size_t)FA_DECODE_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  float* ws = nullptr;
+  if (fa::noalloc_scratch(stream, &ws) != hipSuccess) return FA_ERR_HIP;
+  fa::DecodeArgs a{q,  kcache, vcache, seqlens, offsets, nullptr, 0, 0,
+                   0,  o,      lse,    B,       H,       d,       max_seqlen, scale,
+                   sk, (int)n_splits, ws, nullptr, stream};
+  return fa::launch_decode(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
@@ -289,6 +314,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime refused the launch";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the call needs more than the fixed scratch of fa_decode_varlen_noalloc";
     default: return "unknown fa_status";
   }
 }

@@ -19,8 +19,17 @@
 // otherwise the chunk's state goes to the workspace and the merge kernel
 // combines a sequence's chunk states with the same rule, writing O = u / l
 // and LSE = m + ln l.  Cache row addresses are 64-bit.
+#include <mutex>
+
 #include "cdna4.hpp"
+#include "fa.h"
 #include "kernels.hpp"
+
+// Fixed scratch for fa_decode_varlen_noalloc (callers that cannot allocate):
+// one copy per device, alive until the process ends.  Host code never uses
+// this name as an address; it uses the per-device pointer from
+// hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[FA_DECODE_NOALLOC_SCRATCH_BYTES];
 
 namespace fa {
 
@@ -401,7 +410,38 @@ hipError_t launch_sel(const DecodeArgs& a) {
   return a.counters ? launch<D, PAGED, true>(a) : launch<D, PAGED, false>(a);
 }
 
+constexpr int kMaxScratchDevices = 64;
+
 }  // namespace
+
+hipError_t noalloc_scratch(hipStream_t stream, float** ptr) {
+  static void* table[kMaxScratchDevices];
+  static std::mutex lock;
+  hipDevice_t dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(lock);
+  if (!table[dev]) {
+    // Set-up, once per device, with that device current: the device address
+    // of this device's copy of `scratch`.
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    table[dev] = p;
+  }
+  *ptr = static_cast<float*>(table[dev]);
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a) {
   if (a.block_table)

@@ -80,6 +80,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a);      // d = 128 here, d = 64 below
 hipError_t launch_fwd_bf16_d64(const FwdArgs& a);  // fwd_bf16_d64.hip
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+// Device address of the fixed decode scratch on the stream's device (set up
+// on the first call per device).
+hipError_t noalloc_scratch(hipStream_t stream, float** ptr);
 
 // Workgroup counts, so the host can reject grids the hardware cannot launch.
 long long fwd_bf16_grid(int B, int H, int Nq);

@@ -12,7 +12,7 @@ from conftest import ROOT, gpu_available
 
 HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
            if h.endswith(".h")]
-OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH = 0, -1, -2, -3, -4, -5
 
 # Fake, suitably aligned device addresses: never dereferenced, because every
 # call below is rejected by the host-side checks (or, without a GPU, by the
@@ -48,7 +48,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR):
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH):
         assert fa.fa_status_string(s).startswith("FA_")
     assert "unknown" in fa.fa_status_string(12345)
 
@@ -180,6 +180,26 @@ def test_workspace_and_split_plan():
     assert fa.fa_decode_workspace_bytes(0, 5, 64, 1000) == 0
 
 
+def noalloc_call(q=A, kc=A, vc=A, sl=A2, off=A2, o=A2, lse=A2, B=2, H=4, d=128, max_seqlen=100,
+                 scale=0.1):
+    lib = fa.load()
+    return lib.fa_decode_varlen_noalloc(q, kc, vc, sl, off, o, lse, B, H, d, max_seqlen, scale, None)
+
+
+def test_noalloc_decode_rejects_invalid_arguments():
+    for kw in ("q", "kc", "vc", "sl", "off", "o", "lse"):
+        assert noalloc_call(**{kw: None}) == INVALID
+    assert noalloc_call(kc=A + 4) == INVALID
+    for bad in ({"B": 0}, {"H": 0}, {"max_seqlen": 0}, {"B": 70000}, {"scale": float("inf")}):
+        assert noalloc_call(**bad) == INVALID
+    assert noalloc_call(d=96) == UNSUPPORTED
+    # the fixed scratch is 16 MiB of chunk states: 64 sequences x 32 heads of
+    # 16384 keys fit (8 chunks of 2048 keys), 2048 x 128 heads do not
+    assert 64 * 32 * 8 * 130 * 4 <= 16 << 20
+    assert noalloc_call(B=2048, H=128, max_seqlen=100000) == SCRATCH
+    assert noalloc_call(B=1024, H=64, d=64, max_seqlen=1 << 20) == SCRATCH
+
+
 @pytest.mark.skipif(gpu_available(), reason="uses fake device pointers; only safe with no GPU")
 def test_valid_call_without_gpu_reports_hip_error():
     # All checks pass, so the launch reaches the HIP runtime, which has no
@@ -188,6 +208,7 @@ def test_valid_call_without_gpu_reports_hip_error():
     assert fwd_call("fa_fwd_f32", d=128, causal=1) == HIPERR
     assert dec_call() == HIPERR
     assert dec_split_call(split_keys=128) == HIPERR
+    assert noalloc_call(B=64, H=32, max_seqlen=16384) == HIPERR
 
 
 def test_binding_validates_tensors():
