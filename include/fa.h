@@ -74,7 +74,8 @@ typedef enum {
  *   v   bf16 [B, H, Nk, d]  contiguous (device)
  *   o   bf16 [B, H, Nq, d]  contiguous, written (device)
  *   lse fp32 [B, H, Nq]     written (device)
- *   d in {64, 128}; B, H, Nq, Nk >= 1; scale finite (usually 1/sqrt(d));
+ *   d in {64, 128}; B, H, Nq, Nk >= 1; Nq, Nk <= 2^30 (longer sequences
+ *   return FA_ERR_INVALID_ARG); scale finite (usually 1/sqrt(d));
  *   causal != 0 applies the bottom-right causal mask and skips key tiles that
  *   lie wholly above the diagonal (explainer §6).
  *
@@ -156,7 +157,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  *                 sequence b owns rows cu[b] .. cu[b+1]-1
  *   total_q       query rows (host); max_seqlen_q an upper bound of every
  *                 sequence's query count (host; sizes the grid, no device
- *                 read on the host), 1 <= max_seqlen_q <= total_q
+ *                 read on the host), 1 <= max_seqlen_q <= min(total_q, 2^30)
  *   d             64 or 128
  *
  * A query row that sees no key gets O = 0 and LSE = -inf.  Errors as for
@@ -188,6 +189,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  *   lse      fp32 [B, H]           written (device)
  *   max_seqlen  an upper bound of seqlens[] (host; sizes the grid, so no
  *               device-to-host copy is needed); 0 <= seqlens[b] <= max_seqlen
+ *               <= 2^30; B and H at most 65535
  *   workspace   device scratch of at least fa_decode_workspace_bytes(B, H, d,
  *               max_seqlen) bytes, owned by the caller.  Its first 65536 bytes
  *               are arrival counters: they must be ZERO before the first call

@@ -87,6 +87,40 @@ def load():
     return _lib
 
 
+def load_library(path):
+    """Another build of the library (e.g. the race-check build
+    libfa_paranoid.so), loaded beside the default one with the same
+    signatures; use it through `using_library`."""
+    import torch  # noqa: F401
+
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+class using_library:
+    """Context manager: the functions of this module call `lib` inside it."""
+
+    def __init__(self, lib):
+        self.lib = lib
+
+    def __enter__(self):
+        global _lib
+        self.saved = load()
+        _lib = self.lib
+        return self.lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
 def fa_status_string(status: int) -> str:
     return load().fa_status_string(int(status)).decode()
 

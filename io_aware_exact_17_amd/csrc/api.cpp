@@ -29,11 +29,19 @@ constexpr long long kMaxChunkPages = 1024;    // pages one chunk may span (stage
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Longest sequence any entry point accepts (query or key count, decode
+// history).  Kernel index arithmetic is 32-bit; with lengths up to 2^30 every
+// position, tile bound and row offset within a head stays far from overflow.
+constexpr long long kMaxLen = 1LL << 30;
+
 bool dims_ok(int B, int H, int Nq, int Nk) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return false;
+  if (Nq > kMaxLen || Nk > kMaxLen) return false;
   if ((long long)B * H > INT_MAX) return false;
   return true;
 }
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int Nq, int Nk, int d, float scale, int causal, hipStream_t stream, bool f32) {
@@ -59,11 +67,20 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
 // keys read at 6.34 / 6.42 / 6.38 / 6.23 TB/s; the one-sequence case is
 // fastest at 256.)
 int choose_split_keys(int B, int H, int max_seqlen) {
+  const long long bh = (long long)B * H;  // B, H >= 1; B * H * chunks > 16384 <=> chunks > 16384 / bh
   long long sk = 256;
-  while (sk < max_seqlen && ((long long)B * H * ((max_seqlen + sk - 1) / sk) > 16384 ||
-                             (max_seqlen + sk - 1) / sk > kPlanChunks))
+  while (sk < max_seqlen &&
+         (ceil_div(max_seqlen, sk) > 16384 / bh || ceil_div(max_seqlen, sk) > kPlanChunks))
     sk *= 2;
   return (int)sk;
+}
+
+// Shapes every decode entry point and sizing function accepts (the grid
+// holds H and B in its x and z dimensions; every size product then fits in
+// 64 bits).
+bool decode_dims_ok(int B, int H, long long max_seqlen) {
+  return B >= 1 && H >= 1 && B <= kMaxGridYZ && H <= kMaxGridYZ && max_seqlen >= 1 &&
+         max_seqlen <= kMaxLen;
 }
 
 bool page_size_ok(int page_size) {
@@ -114,7 +131,7 @@ int decode_packed(const void* q, const void* kcache, const void* vcache, const i
   if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned4(o) ||
       !aligned4(lse) || !aligned4(seqlens) || !aligned4(offsets))
     return FA_ERR_INVALID_ARG;
-  if (B < 1 || H < 1 || max_seqlen < 1) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || max_seqlen < 1 || max_seqlen > kMaxLen) return FA_ERR_INVALID_ARG;
   if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_INVALID_ARG;  // grid.z / grid.x
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (split_keys < 0) return FA_ERR_INVALID_ARG;
@@ -137,7 +154,7 @@ extern "C" {
 
 int fa_decode_paged_split_keys(int B, int H, int d, int max_seqlen, int page_size) {
   (void)d;
-  if (B < 1 || H < 1 || max_seqlen < 1 || !page_size_ok(page_size)) return 0;
+  if (!decode_dims_ok(B, H, max_seqlen) || !page_size_ok(page_size)) return 0;
   return choose_paged_split_keys(B, H, max_seqlen, page_size);
 }
 
@@ -159,6 +176,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
       !aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k))
     return FA_ERR_INVALID_ARG;
   if (B < 1 || B > kMaxGridYZ || H < 1 || total_q < 1 || max_seqlen_q < 1) return FA_ERR_INVALID_ARG;
+  if (max_seqlen_q > kMaxLen) return FA_ERR_INVALID_ARG;
   if ((long long)B * H > INT_MAX) return FA_ERR_INVALID_ARG;
   if (max_seqlen_q > total_q) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
@@ -184,12 +202,12 @@ int fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, fl
   if (!dims_ok(B, H, Nq, Nk)) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (d != 128) return FA_ERR_UNSUPPORTED;
-  if ((Nk + kSparseBlock - 1) / kSparseBlock > kMaxSparseKeyBlocks) return FA_ERR_INVALID_ARG;
+  if (ceil_div(Nk, kSparseBlock) > kMaxSparseKeyBlocks) return FA_ERR_INVALID_ARG;
   if (fa::fwd_bf16_grid(B, H, Nq) > kMaxGridX) return FA_ERR_INVALID_ARG;
   fa::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal ? 1 : 0, stream};
   a.bmask = block_mask;
-  a.nqb = (Nq + kSparseBlock - 1) / kSparseBlock;
-  a.nkb = (Nk + kSparseBlock - 1) / kSparseBlock;
+  a.nqb = (int)ceil_div(Nq, kSparseBlock);
+  a.nkb = (int)ceil_div(Nk, kSparseBlock);
   return fa::launch_fwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -220,12 +238,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 
 int fa_decode_split_keys(int B, int H, int d, int max_seqlen) {
   (void)d;
-  if (B < 1 || H < 1 || max_seqlen < 1) return 0;
+  if (!decode_dims_ok(B, H, max_seqlen)) return 0;
   return choose_split_keys(B, H, max_seqlen);
 }
 
 size_t fa_decode_split_workspace_bytes(int B, int H, int d, int max_seqlen, int split_keys) {
-  if (B < 1 || H < 1 || max_seqlen < 1 || (d != 64 && d != 128) || split_keys < 0) return 0;
+  if (!decode_dims_ok(B, H, max_seqlen) || (d != 64 && d != 128) || split_keys < 0) return 0;
   const long long sk = split_keys > 0 ? split_keys : choose_split_keys(B, H, max_seqlen);
   if (!chunking_ok(max_seqlen, sk, 0)) return 0;
   return split_workspace_bytes(B, H, d, max_seqlen, sk);
@@ -262,6 +280,7 @@ int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
       !aligned4(lse) || !aligned4(seqlens) || !aligned4(block_table))
     return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || max_seqlen < 1 || num_pages < 1 || max_blocks < 1) return FA_ERR_INVALID_ARG;
+  if (max_seqlen > kMaxLen) return FA_ERR_INVALID_ARG;
   if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_INVALID_ARG;  // grid.z / grid.x
   if (!page_size_ok(page_size)) return FA_ERR_INVALID_ARG;
   if ((long long)max_blocks * page_size < max_seqlen) return FA_ERR_INVALID_ARG;
@@ -289,7 +308,7 @@ int fa_decode_varlen_noalloc(const void* q, const void* kcache, const void* vcac
   if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned4(o) ||
       !aligned4(lse) || !aligned4(seqlens) || !aligned4(offsets))
     return FA_ERR_INVALID_ARG;
-  if (B < 1 || H < 1 || max_seqlen < 1) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || max_seqlen < 1 || max_seqlen > kMaxLen) return FA_ERR_INVALID_ARG;
   if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;

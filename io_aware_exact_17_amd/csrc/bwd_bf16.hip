@@ -327,6 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
   for (int qb = qb_first; qb < n_qb; ++qb) {
     const int buf = (qb - qb_first) & (kDkdvBufs - 1);
+    paranoid_sync();
     {
       const lds_char* qt = q_tile(buf);
       const lds_char* dt = do_tile(buf);
@@ -429,6 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       }
     }
     if ((qb - qb_first) % kDkdvAhead == kDkdvAhead - 1 && qb + 1 < n_qb) __syncthreads();
+    paranoid_sync();
   }
 
   // dK^T / dV^T accumulators: lane = key, register r of dim block db =
@@ -531,7 +533,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   }
   for (int kb = 0; kb < n_kb; ++kb) {
     const int buf = kb & (kDqBufs - 1);
+    paranoid_sync();
     if (kb + 2 < n_kb) stage(kb + 2, (kb + 2) & (kDqBufs - 1));
+    paranoid_sync();
     {  // blocks past this wave's last visible key are masked whole
       const lds_char* kt_ = k_tile(buf);
       const lds_char* vt = v_tile(buf);
@@ -651,7 +655,7 @@ hipError_t launch(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   {
-    const int n_kt = (a.Nk + kFixed - 1) / kFixed;
+    const int n_kt = (int)(((long long)a.Nk + kFixed - 1) / kFixed);
     void* args[] = {(void*)&a.q,  (void*)&a.k,  (void*)&a.v,  (void*)&a.dout, (void*)&lse2,
                     (void*)&Dv,   (void*)&a.dk, (void*)&a.dv, (void*)&BH,     (void*)&a.Nq,
                     (void*)&a.Nk, (void*)&c,    (void*)&a.scale};
@@ -660,7 +664,7 @@ hipError_t launch(const BwdArgs& a) {
                                          a.stream);
     if (e != hipSuccess) return e;
   }
-  const int n_qt = (a.Nq + kFixed - 1) / kFixed;
+  const int n_qt = (int)(((long long)a.Nq + kFixed - 1) / kFixed);
   void* args[] = {(void*)&a.q,  (void*)&a.k,  (void*)&a.v,  (void*)&a.dout, (void*)&lse2,
                   (void*)&Dv,   (void*)&a.dq, (void*)&BH,   (void*)&a.Nq,   (void*)&a.Nk,
                   (void*)&c,    (void*)&a.scale, (void*)&n_qt};
@@ -676,7 +680,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a) {
 }
 
 long long bwd_bf16_grid(int B, int H, int N) {
-  return (long long)((N + kFixed - 1) / kFixed) * B * H;
+  return (((long long)N + kFixed - 1) / kFixed) * B * H;
 }
 
 }  // namespace fa

@@ -94,6 +94,19 @@ __device__ __forceinline__ void copy_to_lds(const char* gbase, uint32_t voff, ui
 #pragma clang diagnostic pop
 }
 
+// Race-check build (compiled with FA_PARANOID_SYNC): at every point where a
+// kernel moves from one LDS stage to the next, every memory operation of the
+// wave completes (vmcnt, expcnt and lgkmcnt all zero) and the workgroup meets
+// at a barrier.  Nothing is then in flight across a stage boundary, so a
+// missing or miscounted wait in the normal build shows up as a difference
+// between the two builds' results.  A no-op in the normal build.
+__device__ __forceinline__ void paranoid_sync() {
+#ifdef FA_PARANOID_SYNC
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#endif
+}
+
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
 }

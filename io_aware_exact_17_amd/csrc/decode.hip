@@ -346,8 +346,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     // The state has reached the coherence point before the arrival counts.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     uint32_t seen = 0;
+#ifdef FA_PARANOID_SYNC
+    // race-check build: full device-scope release / acquire around the count
+    __threadfence();
+    if (lane == 0)
+      seen = __hip_atomic_fetch_add(counters + bh, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    __threadfence();
+#else
     if (lane == 0)
       seen = __hip_atomic_fetch_add(counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#endif
     seen = __builtin_amdgcn_readfirstlane(seen);
     if (seen != (uint32_t)(n_active - 1)) return;  // another chunk is still running
     // Last to arrive: every other chunk's state is in place.  Reset the

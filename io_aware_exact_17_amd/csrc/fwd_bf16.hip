@@ -688,8 +688,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     using NKB = std::integral_constant<int, (U + 2) % kNBuf>;
     using NVB = std::integral_constant<int, (U + 1) % kNBuf>;
     const bool more_k = j + 4 < n_tiles, more_v = j + 3 < n_tiles;
+    paranoid_sync();
     if (more_k) issue_k(std::integral_constant<int, U>{}, j + 4);
     if (more_v) issue_v(std::integral_constant<int, (U + 3) % kNBuf>{}, j + 3);
+    paranoid_sync();
     if (j < njw) {
       step(KB{}, VB{}, H0{}, KB{}, VB{}, H1{}, 2 * j + 1, ops, sB, sA, pB, pA);
       step(KB{}, VB{}, H1{}, NKB{}, NVB{}, H0{}, 2 * j + 2, ops, sA, sB, pA, pB);
@@ -826,7 +828,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
 template <int D, bool CAUSAL, bool VARLEN, bool SPARSE>
 hipError_t launch(const FwdArgs& a) {
-  const int n_qtiles = (a.Nq + kBR - 1) / kBR;
+  const int n_qtiles = (int)(((long long)a.Nq + kBR - 1) / kBR);
   const int BH = a.B * a.H;
   // Scores enter the exponent as s * c (log2 units); masking acts on P,
   // so c may have either sign or be zero.
@@ -852,7 +854,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a) {
 }
 
 long long fwd_bf16_grid(int B, int H, int Nq) {
-  return (long long)((Nq + kBR - 1) / kBR) * B * H;
+  return (((long long)Nq + kBR - 1) / kBR) * B * H;
 }
 
 }  // namespace fa

@@ -531,10 +531,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   for (int p = 0; cur.item < n_items || prv.item < n_items; ++p) {
     const bool have_cur = cur.item < n_items;
     const Item& ic = cur.it;
+    paranoid_sync();
     if (ld.item < n_items) {
       issue_tile(ld, p + 2);
       advance(ld);
     }
+    paranoid_sync();
     if (!group_b) {
       if (have_cur) {
         prefetch_q(cur);
@@ -596,7 +598,7 @@ hipError_t cu_count(hipStream_t stream, int* cus) {
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdArgs& a) {
-  const int n_qtiles = (a.Nq + kBR - 1) / kBR;
+  const int n_qtiles = (int)(((long long)a.Nq + kBR - 1) / kBR);
   const int BH = a.B * a.H;
   // c > 0 keeps masked scores (-inf) at -inf after scaling.  A zero scale
   // becomes 1e-30: every product with a finite score then rounds away

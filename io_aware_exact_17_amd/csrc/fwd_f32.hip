@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a) {
-  const int n_qtiles = (a.Nq + kBR - 1) / kBR;
+  const int n_qtiles = (int)(((long long)a.Nq + kBR - 1) / kBR);
   const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
   void* args[] = {(void*)&a.q, (void*)&a.k, (void*)&a.v, (void*)&a.o, (void*)&a.lse,
@@ -125,7 +125,7 @@ hipError_t launch_fwd_f32(const FwdArgs& a) {
 }
 
 long long fwd_f32_grid(int B, int H, int Nq) {
-  return (long long)((Nq + kBR - 1) / kBR) * B * H;
+  return (((long long)Nq + kBR - 1) / kBR) * B * H;
 }
 
 }  // namespace fa

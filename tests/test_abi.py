@@ -77,6 +77,10 @@ def test_fwd_rejects_invalid_arguments(entry):
         assert fwd_call(entry, d=d) == UNSUPPORTED
     # grid of more than 2^31 - 1 workgroups
     assert fwd_call(entry, B=65535, H=65535 // 2, Nq=1 << 20) == INVALID
+    # sequences longer than 2^30 (kernel index arithmetic is 32-bit)
+    assert fwd_call(entry, Nq=(1 << 30) + 1) == INVALID
+    assert fwd_call(entry, Nk=(1 << 30) + 1) == INVALID
+    assert fwd_call(entry, Nq=2**31 - 1, Nk=2**31 - 1) == INVALID
 
 
 def varlen_call(q=A, k=A, v=A, o=A2, lse=A2, cq=A2, ck=A2, B=2, H=4, d=64, total_q=100,
@@ -144,6 +148,10 @@ def test_decode_rejects_invalid_arguments():
         assert dec_call(**bad) == INVALID
         assert dec_split_call(**bad) == INVALID
     assert dec_call(scale=float("nan")) == INVALID
+    assert dec_call(max_seqlen=(1 << 30) + 1) == INVALID
+    assert fa.fa_decode_split_keys(1, 1, 128, (1 << 30) + 1) == 0
+    assert fa.fa_decode_workspace_bytes(65536, 1, 128, 100) == 0
+    assert fa.fa_decode_split_keys(2**31 - 1, 2**31 - 1, 128, 1 << 20) == 0
     assert dec_split_call(split_keys=0) == INVALID     # the split entry needs an explicit size
     assert dec_split_call(split_keys=-64) == INVALID
     assert dec_split_call(split_keys=100) == INVALID   # not a multiple of 64
