@@ -17,7 +17,7 @@
 //    products run on the matrix cores as v_mfma_f32_32x32x16_bf16; every K or
 //    V operand read from LDS feeds both row blocks, which halves the LDS read
 //    traffic per matrix instruction against 32-row waves.  O^T lives in the
-//    accumulation registers, and so does Q (loaded there directly).
+//    accumulation registers, and so does Q.
 //  * The score block is formed transposed, S^T = K Q^T, so every lane holds
 //    one query column: row max and row sum are in-lane reductions plus one
 //    exchange between lane halves (v_permlane32_swap); no reduction crosses
@@ -49,10 +49,18 @@
 //    The mathematics is unchanged: the final division uses the same
 //    reference.  Masks (causal diagonal, keys past the end) act on P, so they
 //    are exact whatever the sign of the scale.
-//  * Workgroups are issued heaviest query tile first; consecutive workgroup
-//    ids walk the heads, so when B*H is a multiple of 8 every tile of a head
-//    lands on the same XCD (workgroups are dealt round-robin to the 8 XCDs)
-//    and shares its K/V in that XCD's L2.
+//  * Work items (head, query tile) are listed heaviest query tile first,
+//    heads fastest.  Dense: one workgroup per CU, each taking one item per
+//    round of G (the CU count) as one stream of tile positions: the K/V
+//    copies run ahead across item boundaries, the next item's Q is requested
+//    at the end of the item before, and O leaves through the LDS freed by
+//    the last V tile, so the pipeline fills once per workgroup, not once per
+//    query tile.  Odd rounds go in reverse order of 8-workgroup blocks, which
+//    pairs heavy and light causal tiles on every CU.  Workgroups are dealt
+//    round-robin to the 8 XCDs, so with G and B*H multiples of 8 every item
+//    of a head lands on the same XCD and shares its K/V in that XCD's L2.
+//    Varlen and block-sparse launch one workgroup per item, which the
+//    hardware balances over sequences of any length or sparsity.
 #include "cdna4.hpp"
 #include "kernels.hpp"
 
@@ -115,12 +123,16 @@ __device__ __forceinline__ void qk_first(f32x16& d, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void qk_next(f32x16& d, bf16x8 a, bf16x8 b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
-// 16 bytes from global memory into four accumulation registers.  The
-// compiler does not track this load; the caller waits for it (vmcnt).
-__device__ __forceinline__ bf16x8 load_to_acc(const bf16* p) {
-  bf16x8 r;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(r) : "v"(p) : "memory");
-  return r;
+// Wait until at most the vector-memory operations a tile iteration issued
+// are outstanding: its own K and V tile copies (IPW instructions each, if
+// issued).  Operations complete in issue order, so everything older has
+// then landed.
+template <int IPW>
+__device__ __forceinline__ void wait_vm(bool k, bool v) {
+  const int kv = (k ? 1 : 0) + (v ? 1 : 0);
+  if (kv == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPW));
+  else if (kv == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // Scheduling pattern: N matrix instructions, each followed by its share of
@@ -186,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int Nq_dense, int Nk_dense,
     float c, int n_qtiles, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
-    int H, int total_q, const uint8_t* __restrict__ bmask, int nqb, int nkb) {
+    int H, int total_q, const uint8_t* __restrict__ bmask, int nqb, int nkb, int n_items) {
   using C = FwdCfg<D>;
   using Ops = QuarterOps<D>;
   constexpr int TB = C::TILE * 2;        // bytes per K or V tile
@@ -194,7 +206,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   constexpr int ROWB = D * 2;            // bytes per tile row
   constexpr int KQ = C::KS / 4;          // k-steps per quarter
   constexpr int VQ = C::NDB / 2;         // dim blocks per quarter
-  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * kNBuf * C::TILE];
+  // K buffers, V buffers and (streaming) 16 KB more, which with V buffer 3
+  // stages O at an item's end.
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * kNBuf * C::TILE + (!VARLEN && !SPARSE ? C::TILE : 0)];
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
@@ -203,9 +217,43 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int col = lane & 31;   // query column of this lane in S^T / O^T
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group this lane holds
 
-  // Heaviest query tile first; heads vary fastest.
-  int qt, Nq, Nk, head;
-  size_t qbase, kbase, lse_base;  // elements
+  // Work items.  Varlen and block-sparse: one item per workgroup, from the
+  // grid.  Dense (STREAM): item it is query tile n_qtiles-1-it/BH of
+  // (batch, head) it%BH -- heaviest first, heads fastest -- and workgroup g
+  // of G (one per CU) takes item rG+g in round r, with odd rounds reversed
+  // in blocks of 8 workgroups (rG+G-8-(g&~7)+(g&7): g mod 8, and so the XCD
+  // that holds a head's K/V in its L2, is kept).  Its items form one stream
+  // of 64-key tile positions; the K/V copies run ahead across item
+  // boundaries and the next item's Q is requested at the end of the item
+  // before, so the pipeline fills once per workgroup, not once per query
+  // tile.
+  constexpr bool STREAM = !VARLEN && !SPARSE;
+  const int G = (int)gridDim.x;
+  const int g = (int)blockIdx.x;
+  auto item_at = [&](int r) -> long long {
+    const int o = ((r & 1) && (G & 7) == 0) ? G - 8 - (g & ~7) + (g & 7) : g;
+    return (long long)r * G + o;
+  };
+  auto valid_round = [&](int r) -> bool { return item_at(r) < n_items; };
+  // Row strides in global memory (a head's rows are contiguous when dense).
+  const size_t q_rs = VARLEN ? (size_t)H * D : (size_t)D;       // elements
+  const uint32_t kv_rsb = VARLEN ? (uint32_t)(H * ROWB) : ROWB;  // bytes
+
+  int qt = 0, Nq = Nq_dense, Nk = Nk_dense, head = 0;
+  size_t qbase = 0, kbase = 0, lse_base = 0;  // elements
+  // Key tiles an item's query tile reaches (dense).
+  auto tiles_of_qt = [&](int t) -> int {
+    const int kv_end = CAUSAL ? min(Nk, t * kBR + kBR + (Nk - Nq)) : Nk;
+    return kv_end > 0 ? (kv_end + kBC - 1) / kBC : 0;
+  };
+  auto set_dense_item = [&](int it) {
+    qt = n_qtiles - 1 - it / BH;
+    const int bh = it % BH;
+    head = bh % max(H, 1);
+    qbase = (size_t)bh * Nq * D;
+    kbase = (size_t)bh * Nk * D;
+    lse_base = (size_t)bh * Nq;
+  };
   if constexpr (VARLEN) {
     // One sequence after another (grid.y), so the workgroups running
     // together share that sequence's K/V in L2; within it, heaviest tile
@@ -221,42 +269,36 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     qbase = ((size_t)qs * H + h) * D;
     kbase = ((size_t)ks * H + h) * D;
     lse_base = (size_t)h * total_q + qs;
+  } else if constexpr (SPARSE) {
+    set_dense_item(g);
   } else {
-    qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
-    const int bh = (int)(blockIdx.x % BH);
-    head = bh % max(H, 1);
-    Nq = Nq_dense;
-    Nk = Nk_dense;
-    qbase = (size_t)bh * Nq * D;
-    kbase = (size_t)bh * Nk * D;
-    lse_base = (size_t)bh * Nq;
+    set_dense_item((int)item_at(0));
   }
-  // Row strides in global memory (a head's rows are contiguous when dense).
-  const size_t q_rs = VARLEN ? (size_t)H * D : (size_t)D;       // elements
-  const uint32_t kv_rsb = VARLEN ? (uint32_t)(H * ROWB) : ROWB;  // bytes
-  const int q0 = qt * kBR;
   const int off = Nk - Nq;  // bottom-right causal alignment
-
-  const int kv_end = CAUSAL ? min(Nk, q0 + kBR + off) : Nk;
-  const int n_cand = kv_end > 0 ? (kv_end + kBC - 1) / kBC : 0;  // key tiles in causal reach
-
-  const int wq0 = q0 + wave * 64;  // first query row of this wave
-  const int qi0 = wq0 + col;       // this lane's row in row block 0 (+32 in block 1)
-  const int kv_end_w = CAUSAL ? min(Nk, wq0 + 64 + off) : Nk;
+  int q0, kv_end, n_cand, wq0, qi0, kv_end_w;
+  auto set_rows = [&]() {
+    q0 = qt * kBR;
+    kv_end = CAUSAL ? min(Nk, q0 + kBR + off) : Nk;
+    n_cand = kv_end > 0 ? (kv_end + kBC - 1) / kBC : 0;  // key tiles in causal reach
+    wq0 = q0 + wave * 64;  // first query row of this wave
+    qi0 = wq0 + col;       // this lane's row in row block 0 (+32 in block 1)
+    kv_end_w = CAUSAL ? min(Nk, wq0 + 64 + off) : Nk;
+  };
+  set_rows();
 
   // Q^T operands: lane holds Q[row][16s + 8*half + 0..7] of both row blocks.
-  // Rows past Nq read row Nq-1 (their results are never stored).
-  // They are loaded straight into accumulation registers, where only the
-  // S^T products read them; the first wait on vector memory (the block mask
-  // read below, or the wait before the first barrier) covers these loads,
-  // which are issued first so that their latency overlaps the mask read.
+  // Rows past Nq read row Nq-1 (their results are never stored).  They live
+  // in accumulation registers, where only the S^T products read them.
   bf16x8 qf[2][C::KS];
+  auto load_q = [&](bf16x8 (&dst)[2][C::KS], size_t qb, int first_row) {
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const bf16* src = Q + qbase + (size_t)min(qi0 + 32 * rb, Nq - 1) * q_rs + 8 * half;
+    for (int rb = 0; rb < 2; ++rb) {
+      const bf16* src = Q + qb + (size_t)min(first_row + col + 32 * rb, Nq - 1) * q_rs + 8 * half;
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) qf[rb][s] = load_to_acc(src + 16 * s);
-  }
+      for (int s = 0; s < C::KS; ++s) dst[rb][s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
+    }
+  };
+  load_q(qf, qbase, wq0);
 
   // Block-sparse: the list of key tiles (s_tile) that any of the four mask
   // rows of the workgroup admits, in order, with the admitting waves as bits
@@ -300,11 +342,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     }
     njw = cnt;
     nbw = 2 * njw;
-  } else {
+  }
+  auto set_wave_blocks = [&]() {
     nbw = kv_end_w > 0 ? (kv_end_w + 31) / 32 : 0;  // 32-key blocks this wave needs
     njw = (nbw + 1) / 2;                             // tiles this wave needs
-  }
-  const int n_tiles = n_list;
+  };
+  if constexpr (!SPARSE) set_wave_blocks();
+  int n_tiles = n_list;
+  int n_pos = STREAM ? (n_tiles + kNBuf - 1) / kNBuf * kNBuf : n_tiles;  // positions of the item
   // Key tile of list entry j (the identity when dense).  The walk also
   // forms the scores of the block after the last one; past the list that is
   // a tile beyond Nk, masked whole as in the dense walk.
@@ -341,8 +386,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const int r = (wave * C::IPW + i) * C::RPI + ld_row;
     g_off[i] = (uint32_t)(r * kv_rsb + swz<D>(r, ld_slot) * 16);  // the permutation is its own inverse
   }
-  const char* const kg = reinterpret_cast<const char*>(K + kbase);
-  const char* const vg = reinterpret_cast<const char*>(V + kbase);
   const uint32_t lds_wave = (uint32_t)(size_t)lds + wave * C::IPW * 1024;
   auto issue = [&](const char* base, int region, int j) {
     const int tj = tile_of(j);
@@ -362,9 +405,45 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       }
     }
   };
-  // Tile j of K and of V both go to buffer j % kNBuf.
-  auto issue_k = [&](auto buf, int j) { issue(kg, decltype(buf)::value * TB, j); };
-  auto issue_v = [&](auto buf, int j) { issue(vg, VREG + decltype(buf)::value * TB, j); };
+  // The tile stream.  Copy position p (counted from the current item's
+  // first position) is the current item's tile p while p < n_pos, else
+  // tile p - n_pos of the next item that has key tiles (nx_bh >= 0: its
+  // batch x head, nx_tiles its key tiles).  Items take a multiple of kNBuf
+  // positions when streaming, so every item starts at buffer 0; positions
+  // past an item's last tile copy nothing.  Position p goes to buffer
+  // p % kNBuf.
+  int nx_bh = -1, nx_tiles = 0;
+  auto find_next = [&](int r) {  // the first item with key tiles from round r on
+    nx_bh = -1;
+    nx_tiles = 0;
+    if constexpr (STREAM) {
+      for (; valid_round(r); ++r) {
+        const int it = (int)item_at(r);
+        const int nt = tiles_of_qt(n_qtiles - 1 - it / BH);
+        if (nt > 0) {
+          nx_bh = it % BH;
+          nx_tiles = nt;
+          return;
+        }
+      }
+    }
+  };
+  auto issue_pos = [&](const bf16* base, int region, int p) -> bool {
+    if (p < n_pos) {
+      if (p >= n_tiles) return false;
+      issue(reinterpret_cast<const char*>(base + kbase), region, p);
+      return true;
+    }
+    if constexpr (STREAM) {
+      p -= n_pos;
+      if (nx_bh < 0 || p >= nx_tiles) return false;
+      issue(reinterpret_cast<const char*>(base + (size_t)nx_bh * Nk * D), region, p);
+      return true;
+    }
+    return false;
+  };
+  auto issue_k = [&](auto buf, int p) -> bool { return issue_pos(K, decltype(buf)::value * TB, p); };
+  auto issue_v = [&](auto buf, int p) -> bool { return issue_pos(V, VREG + decltype(buf)::value * TB, p); };
 
   // LDS read offsets for buffer 0, first 32-key half of the tile; the
   // buffer, the half and (for V) the 16-key group are immediate offsets,
@@ -671,38 +750,41 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     fixup(b, s_cur, p_cur, lsum);
   };
 
-  // Tile iteration j (buffer U = j % kNBuf) first requests K tile j+4 and V
-  // tile j+3 (into the buffers of K tile j and V tile j-1, whose last readers
-  // passed the previous barrier), then runs the steps around blocks 2j+1 and
-  // 2j+2, which read K tile j+1 and V tile j (and, ahead, the first
-  // operands of K tile j+2 and V tile j+1), and finally waits for all but
-  // its own requests, so K tile j+3 and V tile j+2 are in place for
-  // iteration j+1.
+  // Tile iteration j (buffer U = j % kNBuf) first requests the K tile four
+  // positions and the V tile three positions ahead in the stream (into the
+  // buffers of K tile j and V tile j-1, whose last readers passed the
+  // previous barrier; past the item's end these are the next item's first
+  // tiles), then runs the steps around blocks 2j+1 and 2j+2, which read K
+  // tile j+1 and V tile j (and, ahead, the first operands of K tile j+2 and
+  // V tile j+1), and finally waits for all but its own requests, so the
+  // tiles of positions j+3 (K) and j+2 (V) are in place for iteration j+1.
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
   Ops ops;
-  auto iteration = [&](auto u, int j) {
+  int r_cur = 0;  // round of the item being computed (streaming)
+  auto iteration = [&](auto u, int j, bool tail) {
     constexpr int U = decltype(u)::value;
     using KB = std::integral_constant<int, (U + 1) % kNBuf>;
     using VB = std::integral_constant<int, U>;
     using NKB = std::integral_constant<int, (U + 2) % kNBuf>;
     using NVB = std::integral_constant<int, (U + 1) % kNBuf>;
-    const bool more_k = j + 4 < n_tiles, more_v = j + 3 < n_tiles;
     paranoid_sync();
-    if (more_k) issue_k(std::integral_constant<int, U>{}, j + 4);
-    if (more_v) issue_v(std::integral_constant<int, (U + 3) % kNBuf>{}, j + 3);
+    bool ik, iv;
+    if (!tail) {  // the item's own tiles only
+      ik = j + 4 < n_tiles;
+      iv = j + 3 < n_tiles;
+      if (ik) issue(reinterpret_cast<const char*>(K + kbase), U * TB, j + 4);
+      if (iv) issue(reinterpret_cast<const char*>(V + kbase), VREG + ((U + 3) % kNBuf) * TB, j + 3);
+    } else {  // the item's last positions: its own tiles or the next item's first
+      ik = issue_k(std::integral_constant<int, U>{}, j + 4);
+      iv = issue_v(std::integral_constant<int, (U + 3) % kNBuf>{}, j + 3);
+    }
     paranoid_sync();
     if (j < njw) {
       step(KB{}, VB{}, H0{}, KB{}, VB{}, H1{}, 2 * j + 1, ops, sB, sA, pB, pA);
       step(KB{}, VB{}, H1{}, NKB{}, NVB{}, H0{}, 2 * j + 2, ops, sA, sB, pA, pB);
     }
-    if (more_k) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::IPW));
-    } else if (more_v) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::IPW));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
+    wait_vm<C::IPW>(ik, iv);
     __syncthreads();
   };
 
@@ -711,118 +793,197 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   using B1 = std::integral_constant<int, 1>;
   using B2 = std::integral_constant<int, 2>;
   using B3 = std::integral_constant<int, 3>;
-  if (n_tiles > 0) {
-    // Requests in order: Q (above), K tile 0, V tile 0, K tile 1, V tile 1,
-    // K tile 2.  The block-0 scores need only Q and K tile 0, so the first
-    // barrier waits for those; K tile 3 and V tile 2 (the requests of
-    // "iteration -1") follow it.  The second barrier waits for the rest of
-    // the first five tiles and keeps the first tile iteration's request into
-    // K buffer 0 behind every wave's reads of K tile 0.
-    issue_k(B0{}, 0);
-    issue_v(B0{}, 0);
-    if (n_tiles > 1) {
-      issue_k(B1{}, 1);
-      issue_v(B1{}, 1);
-    }
-    if (n_tiles > 2) issue_k(B2{}, 2);
-    if (n_tiles > 2) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * C::IPW));
-    } else if (n_tiles > 1) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * C::IPW));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::IPW));
-    }
-    __syncthreads();
-    if (n_tiles > 3) issue_k(B3{}, 3);
-    if (n_tiles > 2) issue_v(B2{}, 2);
-    if (nbw > 0) {  // block 0 and the scores of block 1 before the first tile iteration
+  // Requests in order: Q (above), K and V of positions 0 and 1, K of
+  // position 2.  At the first item's start all of them are in place; a
+  // barrier, and then the requests of positions 3 (K) and 2 (V), as a tile
+  // iteration would have made them.
+  paranoid_sync();
+  if constexpr (STREAM) find_next(1);
+  issue_k(B0{}, 0);
+  issue_v(B0{}, 0);
+  issue_k(B1{}, 1);
+  issue_v(B1{}, 1);
+  issue_k(B2{}, 2);
+
+  for (bool first = true;; first = false) {
+    paranoid_sync();
+    // The item's Q has landed once nothing is in flight (the first item's
+    // was requested above, a later item's at the end of the item before).
+    // Redefining qf here keeps the compiler from placing waits for those
+    // loads inside the walk, where the tile copies in flight would turn them
+    // into stalls; on every path to the walk qf is redefined here.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        f32x16(&sacc)[2] = hb ? sB : sA;
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-          const bf16x8 a = *reinterpret_cast<const lds_bf16x8*>(lds + k_off[s] + hb * 32 * ROWB);
-          if (s == 0) {
-            qk_first(sacc[0], a, qf[0][s]);
-            qk_first(sacc[1], a, qf[1][s]);
-          } else {
-            qk_next(sacc[0], a, qf[0][s]);
-            qk_next(sacc[1], a, qf[1][s]);
+      for (int s = 0; s < C::KS; ++s) asm volatile("" : "+a"(qf[rb][s]));
+    if (first) {
+      __syncthreads();
+      issue_k(B3{}, 3);
+      issue_v(B2{}, 2);
+    }
+    if constexpr (STREAM) {
+      if (!first) {
+        // The next item: its K tiles 0-2 and V tiles 0-1 are in place (the
+        // last barrier published them), K tile 3 and V tile 2 are in flight.
+        set_dense_item((int)item_at(r_cur));
+        set_rows();
+        set_wave_blocks();
+        n_tiles = n_cand;
+        n_pos = (n_tiles + kNBuf - 1) / kNBuf * kNBuf;
+        find_next(r_cur + 1);
+      }
+    }
+    if (n_tiles > 0) {
+      if (nbw > 0) {  // block 0 and the scores of block 1 before the first tile iteration
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          f32x16(&sacc)[2] = hb ? sB : sA;
+#pragma unroll
+          for (int s = 0; s < C::KS; ++s) {
+            const bf16x8 a = *reinterpret_cast<const lds_bf16x8*>(lds + k_off[s] + hb * 32 * ROWB);
+            if (s == 0) {
+              qk_first(sacc[0], a, qf[0][s]);
+              qk_first(sacc[1], a, qf[1][s]);
+            } else {
+              qk_next(sacc[0], a, qf[0][s]);
+              qk_next(sacc[1], a, qf[1][s]);
+            }
           }
         }
+        products_done();
+        // Block 0 sets the reference: its exact row maximum over the visible
+        // keys (O and l are still zero, so nothing is rescaled).
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          int room = mask_room(0, rb);
+          // opaque to the compiler: its compares against room would
+          // otherwise be hoisted out of the item loop as 64-bit lane masks
+          // and occupy scalar registers across the whole walk
+          asm volatile("" : "+v"(room));
+          float mx = kNegInf;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            mx = (8 * (r >> 2) + (r & 3) > room) ? mx : fmaxf(mx, sA[rb][r] * c);
+          m_ref[rb] = max_across_halves(mx);
+          const float m_use = m_ref[rb] == kNegInf ? 0.f : m_ref[rb];
+          exp8(std::true_type{}, R0c{}, sA[rb], m_use, room, pA[rb], l_part[rb]);
+          exp8(std::true_type{}, R8c{}, sA[rb], m_use, room, pA[rb], l_part[rb]);
+        }
       }
-      products_done();
-      // Block 0 sets the reference: its exact row maximum over the visible
-      // keys (O and l are still zero, so nothing is rescaled).
+      // Every wave has read K tile 0 before the first iteration requests
+      // the tile four positions ahead into its buffer.
+      __syncthreads();
+      if (nbw > 0) ops = load_ops(B1{}, B0{}, H0{}, std::integral_constant<int, 0>{});
+      for (int j = 0; j < n_pos; j += kNBuf) {
+        const bool tail = STREAM && j + kNBuf == n_pos;  // the last group reaches into the next item
+        iteration(B0{}, j, tail);
+        if (!STREAM && j + 1 >= n_pos) break;
+        iteration(B1{}, j + 1, tail);
+        if (!STREAM && j + 2 >= n_pos) break;
+        iteration(B2{}, j + 2, tail);
+        if (!STREAM && j + 3 >= n_pos) break;
+        iteration(B3{}, j + 3, tail);
+      }
+    }
+
+    products_done();  // the epilogue reads O
+
+    // Epilogue: one division per row, O in bf16, LSE = ln2 * (m + log2 l).
+    if constexpr (STREAM) {
+      // The next item's Q is requested first, so that its latency overlaps
+      // this epilogue (the current Q is no longer read).
+      const bool more = valid_round(r_cur + 1);
+      if (more) {
+        const int nx = (int)item_at(r_cur + 1);
+        load_q(qf, (size_t)(nx % BH) * Nq * D, (n_qtiles - 1 - nx / BH) * kBR + wave * 64);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // The next item's tiles fill the K buffers and V buffers 0-2; V buffer
+      // 3 (its last reader passed the last barrier, and the next item's first
+      // iteration refills it only after a barrier) and the 16 KB after it
+      // give each wave 8 KB: O leaves 32 rows at a time, written row-major
+      // with the 16-byte chunks of row r at slots c ^ (r % 16), read back as
+      // whole rows and stored with 16-byte writes, 1 KB contiguous per wave
+      // instruction.
+      const size_t qb = (size_t)(((int)item_at(r_cur)) % BH) * Nq * D;
+      lds_char* const otile = lds + VREG + 3 * TB + wave * 32 * ROWB;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const int room = mask_room(0, rb);
-        float mx = kNegInf;
+        const float l_tot = sum_across_halves(l_part[rb]);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          mx = (8 * (r >> 2) + (r & 3) > room) ? mx : fmaxf(mx, sA[rb][r] * c);
-        m_ref[rb] = max_across_halves(mx);
-        const float m_use = m_ref[rb] == kNegInf ? 0.f : m_ref[rb];
-        exp8(std::true_type{}, R0c{}, sA[rb], m_use, room, pA[rb], l_part[rb]);
-        exp8(std::true_type{}, R8c{}, sA[rb], m_use, room, pA[rb], l_part[rb]);
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const u32x2 w = {pack_bf16x2(oacc[rb][db][4 * g4] * inv, oacc[rb][db][4 * g4 + 1] * inv),
+                             pack_bf16x2(oacc[rb][db][4 * g4 + 2] * inv, oacc[rb][db][4 * g4 + 3] * inv)};
+            const int chunk = 4 * db + g4;  // dims 32db + 8g .. +7; this lane half holds +4h .. +4h+3
+            *reinterpret_cast<lds_u32x2*>(otile + col * ROWB + ((chunk ^ (col & 15)) * 16) + 8 * half) = w;
+          }
+        const int row = qi0 + 32 * rb;
+        if (half == 0 && row < Nq)
+          LSE[(size_t)(((int)item_at(r_cur)) % BH) * Nq + row] =
+              l_tot > 0.f ? (m_ref[rb] + log2_hw(l_tot)) * kLn2 : kNegInf;
+        // same wave: program order orders these reads after the writes above
+        constexpr int kRowsPerStore = 64 * 16 / ROWB;  // rows covered by 64 lanes x 16 B
+#pragma unroll
+        for (int it = 0; it < 32 / kRowsPerStore; ++it) {
+          const int r = it * kRowsPerStore + lane / C::CPR;
+          const int cc = lane % C::CPR;
+          const u32x4 w = *reinterpret_cast<const lds_u32x4*>(otile + r * ROWB + ((cc ^ (r & 15)) * 16));
+          const int grow = wq0 + 32 * rb + r;
+          if (grow < Nq) *reinterpret_cast<u32x4*>(O + qb + (size_t)grow * q_rs + cc * 8) = w;
+        }
+        // the second row block reuses the region: its writes follow these
+        // reads in program order, and LDS operations of a wave complete in order
       }
-    }
-    if (n_tiles > 3) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::IPW));
-    } else if (n_tiles > 2) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::IPW));
     } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-    __syncthreads();
-    if (nbw > 0) ops = load_ops(B1{}, B0{}, H0{}, std::integral_constant<int, 0>{});
-    for (int j = 0; j < n_tiles; j += kNBuf) {
-      iteration(B0{}, j);
-      if (j + 1 >= n_tiles) break;
-      iteration(B1{}, j + 1);
-      if (j + 2 >= n_tiles) break;
-      iteration(B2{}, j + 2);
-      if (j + 3 >= n_tiles) break;
-      iteration(B3{}, j + 3);
-    }
-  }
-
-  products_done();  // the epilogue reads O
-
-  // Epilogue: one division per row, O in bf16, LSE = ln2 * (m + log2 l).
-  // O leaves through LDS (free after the last barrier): each wave writes its
-  // 64 x D tile row-major into its own 16 KB region, with the 16-byte chunks
-  // of row r at slots c ^ (r % 16), then reads whole rows back and stores
-  // them with 16-byte writes, 1 KB contiguous per wave instruction.
-  lds_char* const otile = lds + wave * 64 * ROWB;
+      // O leaves through LDS (free after the last barrier): each wave writes
+      // its 64 x D tile row-major into its own 16 KB region, with the 16-byte
+      // chunks of row r at slots c ^ (r % 16), then reads whole rows back and
+      // stores them with 16-byte writes, 1 KB contiguous per wave instruction.
+      lds_char* const otile = lds + wave * 64 * ROWB;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = 32 * rb + col;  // row within the wave's tile
-    const float l_tot = sum_across_halves(l_part[rb]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      for (int rb = 0; rb < 2; ++rb) {
+        const int r = 32 * rb + col;  // row within the wave's tile
+        const float l_tot = sum_across_halves(l_part[rb]);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+        for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {pack_bf16x2(oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv),
-                         pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv)};
-        const int chunk = 4 * db + g;  // dims 32db + 8g .. +7; this lane half holds +4h .. +4h+3
-        *reinterpret_cast<lds_u32x2*>(otile + r * ROWB + ((chunk ^ (r & 15)) * 16) + 8 * half) = w;
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const u32x2 w = {pack_bf16x2(oacc[rb][db][4 * g4] * inv, oacc[rb][db][4 * g4 + 1] * inv),
+                             pack_bf16x2(oacc[rb][db][4 * g4 + 2] * inv, oacc[rb][db][4 * g4 + 3] * inv)};
+            const int chunk = 4 * db + g4;  // dims 32db + 8g .. +7; this lane half holds +4h .. +4h+3
+            *reinterpret_cast<lds_u32x2*>(otile + r * ROWB + ((chunk ^ (r & 15)) * 16) + 8 * half) = w;
+          }
+        const int row = qi0 + 32 * rb;
+        if (half == 0 && row < Nq)
+          LSE[lse_base + row] = l_tot > 0.f ? (m_ref[rb] + log2_hw(l_tot)) * kLn2 : kNegInf;
       }
-    const int row = qi0 + 32 * rb;
-    if (half == 0 && row < Nq)
-      LSE[lse_base + row] = l_tot > 0.f ? (m_ref[rb] + log2_hw(l_tot)) * kLn2 : kNegInf;
-  }
-  // Same wave wrote the region, so program order is enough between the
-  // writes and these reads.
-  constexpr int kRowsPerStore = 64 * 16 / ROWB;  // rows covered by 64 lanes x 16 B
+      // Same wave wrote the region, so program order is enough between the
+      // writes and these reads.
+      constexpr int kRowsPerStore = 64 * 16 / ROWB;  // rows covered by 64 lanes x 16 B
 #pragma unroll
-  for (int it = 0; it < 64 / kRowsPerStore; ++it) {
-    const int r = it * kRowsPerStore + lane / C::CPR;
-    const int c = lane % C::CPR;
-    const u32x4 w = *reinterpret_cast<const lds_u32x4*>(otile + r * ROWB + ((c ^ (r & 15)) * 16));
-    const int row = wq0 + r;
-    if (row < Nq) *reinterpret_cast<u32x4*>(O + qbase + (size_t)row * q_rs + c * 8) = w;
+      for (int it = 0; it < 64 / kRowsPerStore; ++it) {
+        const int r = it * kRowsPerStore + lane / C::CPR;
+        const int cc = lane % C::CPR;
+        const u32x4 w = *reinterpret_cast<const lds_u32x4*>(otile + r * ROWB + ((cc ^ (r & 15)) * 16));
+        const int row = wq0 + r;
+        if (row < Nq) *reinterpret_cast<u32x4*>(O + qbase + (size_t)row * q_rs + cc * 8) = w;
+      }
+      break;
+    }
+    // Fresh state for the next item.
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int i = 0; i < C::NDB; ++i) oacc[rb][i] = f32x16{};
+      m_ref[rb] = kNegInf;
+      l_part[rb] = 0.f;
+    }
+    if (!valid_round(++r_cur)) break;
   }
 }
 
@@ -833,13 +994,23 @@ hipError_t launch(const FwdArgs& a) {
   // Scores enter the exponent as s * c (log2 units); masking acts on P,
   // so c may have either sign or be zero.
   const float c = a.scale * kLog2e;
-  const dim3 grid = VARLEN ? dim3((unsigned)(n_qtiles * a.H), (unsigned)a.B)
-                           : dim3((unsigned)(n_qtiles * BH));
+  const int n_items = n_qtiles * BH;
+  // Dense: one workgroup per CU (the LDS and registers of one workgroup
+  // fill a CU), each streaming every G-th item.  Varlen and block-sparse:
+  // one workgroup per item.
+  int G = n_items;
+  if constexpr (!VARLEN && !SPARSE) {
+    int cus = 0;
+    const hipError_t e = cu_count(a.stream, &cus);
+    if (e != hipSuccess) return e;
+    G = min(n_items, cus);
+  }
+  const dim3 grid = VARLEN ? dim3((unsigned)(n_qtiles * a.H), (unsigned)a.B) : dim3((unsigned)G);
   const dim3 block(kThreads);
   void* args[] = {(void*)&a.q,     (void*)&a.k,    (void*)&a.v,  (void*)&a.o,       (void*)&a.lse,
                   (void*)&BH,      (void*)&a.Nq,   (void*)&a.Nk, (void*)&c,         (void*)&n_qtiles,
                   (void*)&a.cu_q,  (void*)&a.cu_k, (void*)&a.H,  (void*)&a.total_q, (void*)&a.bmask,
-                  (void*)&a.nqb,   (void*)&a.nkb};
+                  (void*)&a.nqb,   (void*)&a.nkb,  (void*)&n_items};
   return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL, VARLEN, SPARSE>),
                          grid, block, args, 0, a.stream);
 }

@@ -576,26 +576,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   }
 }
 
-// Compute units of the device `stream` belongs to (the null stream: the
-// current device), read once per device and kept: a device property, not
-// state that changes between calls.
-hipError_t cu_count(hipStream_t stream, int* cus) {
-  static std::atomic<int> cache[kMaxDevices];
-  hipDevice_t dev = 0;
-  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (n <= 0) return hipErrorInvalidDevice;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  *cus = n;
-  return hipSuccess;
-}
-
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdArgs& a) {
   const int n_qtiles = (int)(((long long)a.Nq + kBR - 1) / kBR);
@@ -628,6 +608,26 @@ hipError_t launch(const FwdArgs& a) {
 }
 
 }  // namespace
+
+// Compute units of the device `stream` belongs to (the null stream: the
+// current device), read once per device and kept: a device property, not
+// state that changes between calls.
+hipError_t cu_count(hipStream_t stream, int* cus) {
+  static std::atomic<int> cache[kMaxDevices];
+  hipDevice_t dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n <= 0) return hipErrorInvalidDevice;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  *cus = n;
+  return hipSuccess;
+}
 
 hipError_t launch_fwd_bf16_d64(const FwdArgs& a) {
   if (a.cu_q) return a.causal ? launch<64, true, true>(a) : launch<64, false, true>(a);

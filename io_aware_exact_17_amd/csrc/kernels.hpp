@@ -80,6 +80,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a);      // d = 128 here, d = 64 below
 hipError_t launch_fwd_bf16_d64(const FwdArgs& a);  // fwd_bf16_d64.hip
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+// Compute units of the device the stream belongs to (cached per device).
+hipError_t cu_count(hipStream_t stream, int* cus);
 // Device address of the fixed decode scratch on the stream's device (set up
 // on the first call per device).
 hipError_t noalloc_scratch(hipStream_t stream, float** ptr);
