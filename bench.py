@@ -51,9 +51,9 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBPS = 8000.0      # HBM3E
 # HBM bytes per prefill launch from rocprofv3 FETCH_SIZE + WRITE_SIZE at this
 # workload, each scaled by what the counter reads for a plain 1 GiB copy
-# (FETCH x2.0, WRITE x1.0).  None whenever the prefill kernel has changed
-# since the counters were taken.
-PREFILL_TRAFFIC_BYTES = None
+# (FETCH x2.0, WRITE x1.0): 217857.2 KiB x 2 + 66560 KiB.  None whenever the
+# prefill kernel has changed since the counters were taken.
+PREFILL_TRAFFIC_BYTES = 514328986
 
 
 def parse():
@@ -533,7 +533,7 @@ def main():
                            "allocates no device memory"},
         "dispatch": {"fa_fwd d=128 causal": "fwd_bf16_kernel<128, true, false, false>",
                      "fa_fwd d=64": "fwd_bf16_kernel<64, causal, false> (fwd_bf16_d64.hip)",
-                     "fa_decode_varlen / fa_decode_paged": "decode_split_kernel<128, paged, fused=true>",
+                     "fa_decode_varlen / fa_decode_paged": "single request: decode_split_kernel<128, packed, fused=true>; batched: decode_split_kernel<128, packed|paged, fused=false> + decode_merge_kernel<128>",
                      "fa_fwd_varlen": "fwd_bf16_kernel<128, true, true, false>",
                      "fa_fwd_block_sparse": "fwd_bf16_kernel<128, true, false, true>",
                      "fa_bwd": "bwd_rows_kernel, bwd_dkdv_kernel, bwd_dq_kernel",

@@ -173,10 +173,12 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * (explainer §6: a single query sees its whole history; batched decode mixes
  * history lengths).  Each sequence's keys are cut into chunks that are
  * processed in parallel; each chunk leaves a partial state (m, l, u) in the
- * workspace, and the chunk of a sequence that finishes last merges its
- * sequence's states with the block-merge rule of explainer §3/§7 (a sequence
- * that fits in one chunk is finished on the spot; shapes beyond the fused
- * merge's limits get a second, merging kernel instead).
+ * workspace, and the states of a sequence are merged with the block-merge
+ * rule of explainer §3/§7 (a sequence that fits in one chunk is finished on
+ * the spot).  Calls of at most 4096 chunk workgroups in all (B x H x chunks),
+ * at most 1024 chunks per sequence, are merged by the chunk of each sequence
+ * that finishes last, in the same launch; larger calls get a second, merging
+ * kernel, which costs them less than the last arriver's coherent writes.
  *
  *   q        bf16 [B, H, d]        (device)
  *   kcache   bf16 [T, H, d]        token-major (device)

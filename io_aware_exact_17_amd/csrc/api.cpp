@@ -15,6 +15,13 @@ constexpr long long kMaxGridYZ = 65535;
 constexpr long long kPlanChunks = 256;    // chunks per sequence the automatic plan allows
 constexpr long long kMaxChunks = 4096;    // chunks per sequence the merge kernel combines
 constexpr long long kMaxFusedChunks = 1024;  // ... the last chunk to finish combines
+// Calls with more chunk workgroups than this merge in a second kernel: in a
+// large grid the last-arriver merge costs more than it saves (every chunk
+// then stores its state coherently and waits for the stores before counting
+// in: batched 64 x 32 heads, 16384 workgroups, 1445 us against 1429 us for
+// split + merge kernel; the single 8192-token request, 1024 workgroups, 31.1
+// against 31.0 us, in one process on one box).
+constexpr long long kMaxFusedWorkgroups = 4096;
 // Every decode workspace starts with this many arrival counters (4 bytes
 // each, 64 KiB), zero between calls; chunk states follow.  The region has a
 // fixed size so that no call's chunk states ever land on a counter, whatever
@@ -117,6 +124,7 @@ size_t split_workspace_bytes(int B, int H, int d, long long max_seqlen, long lon
 // head) inside the fixed counter region.
 uint32_t* counters_for(void* workspace, int B, int H, long long n_splits) {
   if ((long long)B * H > kCounterSlots || n_splits > kMaxFusedChunks) return nullptr;
+  if ((long long)B * H * n_splits > kMaxFusedWorkgroups) return nullptr;
   return static_cast<uint32_t*>(workspace);
 }
 float* states_of(void* workspace) {
