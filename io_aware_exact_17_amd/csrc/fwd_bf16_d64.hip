@@ -135,6 +135,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int G = (int)gridDim.x;
   const int rs = VARLEN ? H * D : D;  // elements between consecutive rows of a head
 
+  // Non-causal dense launches whose rounds are whole and whose XCDs' slots
+  // split into whole heads deal every query tile of a head to one XCD in one
+  // round (the slots of an XCD are g mod 8 = x), so the head's K/V is fetched
+  // from HBM once and shared through that XCD's L2 (B=64 H=16 N=1024: HBM
+  // reads ~3x the compulsory Q+K+V before, +15% speed).  Causal launches keep
+  // heaviest-first rounds: mixing a head's unequal query tiles in one round
+  // measured 5-33% slower, depending on the order of the tiles.
+  const bool grouped =
+      !VARLEN && !CAUSAL && (G & 7) == 0 && ((G >> 3) % n_qtiles) == 0 && n_items % G == 0;
+
   // ------------------------------------------------------------- the items
   // An item is kept as a few integers; row bases, lengths and tile counts
   // are derived on use (dense: from the kernel arguments), so the three
@@ -185,8 +195,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       it.nk = cu_k[b + 1] - it.ks;
       return it.qt * kBR < it.nq;
     } else {
-      it.qt = n_qtiles - 1 - i / BH;
-      it.bh = i % BH;
+      if (grouped) {
+        // round r, slot gg of the round (gg mod 8 = the workgroup's XCD): the
+        // G/8 slots of an XCD take the n_qtiles query tiles of G/8/n_qtiles
+        // heads
+        const int r = i / G, gg = i - r * G;
+        const int x = gg & 7, k = gg >> 3;
+        it.qt = k % n_qtiles;
+        it.bh = r * (G / n_qtiles) + x * (G / 8 / n_qtiles) + k / n_qtiles;
+      } else {
+        it.qt = n_qtiles - 1 - i / BH;
+        it.bh = i % BH;
+      }
       return true;
     }
   };
