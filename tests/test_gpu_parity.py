@@ -408,30 +408,37 @@ def test_fwd_varlen_equals_dense(fa, d, causal):
     assert torch.equal(lse.permute(1, 0, 2).reshape(H, B * N), lse2)
 
 
-# d = 64 runs as a stream: one workgroup per CU walks every G-th query tile
-# (G = CU count), carrying its tile pipeline across query tiles.  These shapes
-# have more query tiles than CUs, mixed tile counts and, causally with
-# Nq > Nk, query tiles that see no key at all.
-D64_STREAM = [
+# Dense prefill (d = 64 and d = 128) runs as a stream: one workgroup per CU
+# walks every G-th query tile (G = CU count), carrying its tile pipeline
+# across query tiles.  These shapes have more query tiles than CUs, partial
+# last rounds, mixed tile counts and, causally with Nq > Nk, query tiles that
+# see no key at all; the last two (non-causal, whole rounds) take the d = 64
+# path that deals all query tiles of a head to one XCD in one round.
+STREAM = [
     # B, H, Nq, Nk, causal
     (1, 128, 600, 100, True),
     (2, 100, 300, 333, False),
     (1, 96, 1000, 1000, True),
     (5, 67, 600, 600, True),   # B*H = 335, odd: 1005 query tiles, no head-to-XCD alignment
+    (2, 128, 1024, 1024, False),
+    (1, 64, 2048, 1500, False),
 ]
 
 
-@pytest.mark.parametrize("shape", D64_STREAM, ids=lambda s: "x".join(map(str, s)))
-def test_fwd_d64_stream(fa, shape):
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("shape", STREAM, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_stream(fa, shape, d):
     B, H, Nq, Nk, causal = shape
-    log(f"case d64 stream {shape}")
-    q, k, v = W.prefill_inputs(B, H, Nq, Nk, 64, "bf16", seed=Nq + Nk + H, device="cuda")
+    log(f"case d{d} stream {shape}")
+    q, k, v = W.prefill_inputs(B, H, Nq, Nk, d, "bf16", seed=Nq + Nk + H, device="cuda")
     o, lse = run_fwd(fa, q, k, v, 0.125, causal)
-    O, L = oracle.attention(q, k, v, 0.125, causal)
-    check(o, lse, O, L, TOL_BF16, f"d64 stream {shape}")
-    # A head computed alone (one query tile per workgroup) is bit-identical
-    # to the same head inside the stream: nothing carries over between tiles.
-    for b, h in [(0, 0), (B - 1, H // 2), (B - 1, H - 1)]:
+    heads = [(0, 0), (B - 1, H // 2), (B - 1, H - 1), (B // 2, H // 3)]
+    for b, h in heads:
+        O, L = oracle.head_attention(q[b, h], k[b, h], v[b, h], 0.125, causal)
+        check(o[b, h], lse[b, h], O, L, TOL_BF16, f"d{d} stream {shape} b={b} h={h}")
+    # A head computed alone (a single item) is bit-identical to the same head
+    # inside the stream: nothing carries over between query tiles.
+    for b, h in heads:
         o1, lse1 = run_fwd(fa, q[b:b + 1, h:h + 1].contiguous(), k[b:b + 1, h:h + 1].contiguous(),
                            v[b:b + 1, h:h + 1].contiguous(), 0.125, causal)
         assert torch.equal(o1[0, 0], o[b, h]) and torch.equal(lse1[0, 0], lse[b, h]), (b, h)
