@@ -68,16 +68,22 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
 // Chunk size for split-KV decode: start at 256 keys (one workgroup then
 // streams 128 KiB of K+V at d=128) and double while the grid would exceed
 // 16384 workgroups (64 per CU) or a sequence would have more than 256
-// chunks, so a single long sequence still spreads over every CU while a
-// large batch gets fewer, longer chunks.  (Measured on the 64-sequence,
-// 32-head batch of lengths up to 16384: chunks of 1024 / 2048 / 4096 / 8192
-// keys read at 6.34 / 6.42 / 6.38 / 6.23 TB/s; the one-sequence case is
-// fastest at 256.)
+// chunks, so a large batch gets fewer, longer chunks; with fewer
+// (sequence, head) pairs than CUs, also double while the grid would keep at
+// least one workgroup per CU (256 on this device), so each workgroup streams
+// a long chunk and few partial states are merged.  Measured: the 64-sequence,
+// 32-head batch of lengths up to 16384 reads at 6.34 / 6.42 / 6.38 / 6.23
+// TB/s with chunks of 1024 / 2048 / 4096 / 8192 keys; the 8192-token
+// request with 32 heads takes 32.2 / 29.5 / 28.4 / 27.0 / 38.2 us with chunks
+// of 128 / 256 / 512 / 1024 / 2048 (1024: 8 chunks x 32 heads = 256
+// workgroups).
+constexpr long long kTargetWorkgroups = 256;
 int choose_split_keys(int B, int H, int max_seqlen) {
   const long long bh = (long long)B * H;  // B, H >= 1; B * H * chunks > 16384 <=> chunks > 16384 / bh
   long long sk = 256;
   while (sk < max_seqlen &&
-         (ceil_div(max_seqlen, sk) > 16384 / bh || ceil_div(max_seqlen, sk) > kPlanChunks))
+         (ceil_div(max_seqlen, sk) > 16384 / bh || ceil_div(max_seqlen, sk) > kPlanChunks ||
+          (bh < kTargetWorkgroups && bh * ceil_div(max_seqlen, 2 * sk) >= kTargetWorkgroups)))
     sk *= 2;
   return (int)sk;
 }

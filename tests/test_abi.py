@@ -170,9 +170,13 @@ COUNTER_BYTES = 65536  # arrival counters at the start of every decode workspace
 
 
 def test_workspace_and_split_plan():
-    # a single long sequence is cut into 256-key chunks
-    assert fa.fa_decode_split_keys(1, 32, 128, 8192) == 256
-    assert fa.fa_decode_workspace_bytes(1, 32, 128, 8192) == COUNTER_BYTES + 1 * 32 * 32 * 130 * 4
+    # with fewer (sequence, head) pairs than CUs, chunks as long as still give
+    # every CU a workgroup: 32 heads x 8192 keys -> 8 chunks of 1024
+    assert fa.fa_decode_split_keys(1, 32, 128, 8192) == 1024
+    assert fa.fa_decode_workspace_bytes(1, 32, 128, 8192) == COUNTER_BYTES + 1 * 32 * 8 * 130 * 4
+    assert fa.fa_decode_split_keys(4, 32, 128, 8192) == 4096   # 128 pairs x 2 chunks
+    assert fa.fa_decode_split_keys(1, 1, 128, 65536) == 256    # one pair: 256 chunks
+    assert fa.fa_decode_split_keys(1, 32, 128, 100) == 256
     assert fa.fa_decode_split_workspace_bytes(1, 32, 128, 8192, 0) == fa.fa_decode_workspace_bytes(
         1, 32, 128, 8192)
     # a large batch gets longer chunks, keeping the grid <= 16384 workgroups
