@@ -247,15 +247,22 @@ def cpu_baseline(budget_s: float):
 def read_ceiling(torch, fa, dev, stream, small_bytes):
     """Empirical read bandwidth (GB/s) of a plain streaming-read kernel
     (fa_probe_read) for the single decode's byte count and for 8 GiB, each
-    repetition on a region no earlier repetition touched (cold, clean cache)."""
+    repetition on a region no earlier repetition touched (cold, clean cache).
+    Each timed read is queued behind an untimed 1 GiB read of another region,
+    so the GPU reaches the start event with the timed launch already
+    submitted, as in the bench step (an idle GPU would add the host's launch
+    latency, several microseconds, to a 25 us read)."""
     big = torch.empty(8 << 30, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    filler = big[7 << 30:]  # never timed
 
-    def timed(nbytes, offsets, skip):
+    def timed(nbytes, offsets, skip, fill):
         ts = []
         for i, off in enumerate(offsets):
             e0, e1 = ev(), ev()
+            if fill:
+                fa.fa_probe_read(filler, sink=sink, stream=stream)
             e0.record(stream)
             fa.fa_probe_read(big[off:off + nbytes], sink=sink, stream=stream)
             e1.record(stream)
@@ -264,8 +271,8 @@ def read_ceiling(torch, fa, dev, stream, small_bytes):
                 ts.append(e0.elapsed_time(e1))
         return nbytes / (statistics.mean(ts) * 1e-3) / 1e9
 
-    small = timed(small_bytes, [i * small_bytes for i in range(12)], 2)
-    full = timed(big.numel(), [0, 0, 0], 1)
+    small = timed(small_bytes, [i * small_bytes for i in range(12)], 2, True)
+    full = timed(big.numel(), [0, 0, 0], 1, False)
     del big
     return small, full
 
