@@ -705,15 +705,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     __builtin_amdgcn_sched_group_barrier(0x100, KQ + 2 * VQ, 0);
   };
 
-  // Masking of block b after the fact: P is formed again from the scores
-  // with the keys past lim(rb) cleared (whatever a stale score produced is
-  // dropped), and so are the lane's P sums.
+  // Masking of block b after the fact, per row block: where every row sees
+  // every key (a causal diagonal block is so for one of its two row blocks)
+  // P stands; where no row sees any key (the other row block of the second
+  // diagonal block, the block after the wave's last key, keys past Nk) P and
+  // the P sums are cleared without any arithmetic; otherwise P is formed
+  // again from the scores with the keys past lim(rb) cleared.  Whatever a
+  // stale score produced is dropped.
   auto apply_mask = [&](int b, const f32x16 (&sacc)[2], uint32_t (&pk)[2][8], float (&lsum)[2]) {
     consume(pk, lsum);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int room = mask_room(b, rb);
+      // register 15 holds key 27 (+4 in the upper lane half, already in room)
+      if (!wave_any(room < 27)) continue;
       lsum[rb] = 0.f;
+      if (!wave_any(room >= 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pk[rb][i] = 0u;
+        continue;
+      }
       exp8(std::true_type{}, R0c{}, sacc[rb], m_ref[rb], room, pk[rb], lsum[rb]);
       exp8(std::true_type{}, R8c{}, sacc[rb], m_ref[rb], room, pk[rb], lsum[rb]);
     }
