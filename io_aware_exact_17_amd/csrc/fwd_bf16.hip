@@ -915,8 +915,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       // iteration refills it only after a barrier) and the 16 KB after it
       // give each wave 8 KB: O leaves 32 rows at a time, written row-major
       // with the 16-byte chunks of row r at slots c ^ (r % 16), read back as
-      // whole rows and stored with 16-byte writes, 1 KB contiguous per wave
-      // instruction.
+      // whole rows and stored with 16-byte non-temporal writes, 1 KB
+      // contiguous per wave instruction.  O is not read again by the kernel;
+      // as ordinary writes its lines took L2 room from the K/V tiles the
+      // other workgroups of the XCD re-read (3-5% of the causal rate).
       const size_t qb = (size_t)(((int)item_at(r_cur)) % BH) * Nq * D;
       lds_char* const otile = lds + VREG + 3 * TB + wave * 32 * ROWB;
 #pragma unroll
@@ -944,7 +946,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
           const int cc = lane % C::CPR;
           const u32x4 w = *reinterpret_cast<const lds_u32x4*>(otile + r * ROWB + ((cc ^ (r & 15)) * 16));
           const int grow = wq0 + 32 * rb + r;
-          if (grow < Nq) *reinterpret_cast<u32x4*>(O + qb + (size_t)grow * q_rs + cc * 8) = w;
+          if (grow < Nq) __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(O + qb + (size_t)grow * q_rs + cc * 8));
         }
         // the second row block reuses the region: its writes follow these
         // reads in program order, and LDS operations of a wave complete in order
@@ -953,7 +955,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       // O leaves through LDS (free after the last barrier): each wave writes
       // its 64 x D tile row-major into its own 16 KB region, with the 16-byte
       // chunks of row r at slots c ^ (r % 16), then reads whole rows back and
-      // stores them with 16-byte writes, 1 KB contiguous per wave instruction.
+      // stores them with 16-byte non-temporal writes, 1 KB contiguous per
+      // wave instruction.
       lds_char* const otile = lds + wave * 64 * ROWB;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
@@ -982,7 +985,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         const int cc = lane % C::CPR;
         const u32x4 w = *reinterpret_cast<const lds_u32x4*>(otile + r * ROWB + ((cc ^ (r & 15)) * 16));
         const int row = wq0 + r;
-        if (row < Nq) *reinterpret_cast<u32x4*>(O + qbase + (size_t)row * q_rs + cc * 8) = w;
+        if (row < Nq) __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(O + qbase + (size_t)row * q_rs + cc * 8));
       }
       break;
     }
