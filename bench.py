@@ -51,9 +51,9 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBPS = 8000.0      # HBM3E
 # HBM bytes per prefill launch from rocprofv3 FETCH_SIZE + WRITE_SIZE at this
 # workload, each scaled by what the counter reads for a plain 1 GiB copy
-# (FETCH x2.0, WRITE x1.0): 217857.2 KiB x 2 + 66560 KiB.  None whenever the
+# (FETCH x2.0, WRITE x1.0): 215595.2 KiB x 2 + 66560 KiB.  None whenever the
 # prefill kernel has changed since the counters were taken.
-PREFILL_TRAFFIC_BYTES = 514328986
+PREFILL_TRAFFIC_BYTES = 509696410
 
 
 def parse():
