@@ -64,6 +64,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 
 constexpr int kThreads = 512;
 constexpr int kBR = 256;          // query rows per workgroup (8 waves x 32)
@@ -84,7 +86,8 @@ struct FwdCfg {
   static constexpr int TILE = BC * ROWB;            // bytes per K or V tile
   static constexpr int RPI = 1024 / ROWB;           // tile rows per 1 KB wave instruction
   static constexpr int IPW = TILE / 1024 / (kThreads / 64);  // wave instructions per tile per wave
-  static constexpr int LDS_BYTES = (kKBuf + kVBuf) * TILE;
+  static constexpr int OST = 2048;  // per-wave O staging (16 rows)
+  static constexpr int LDS_BYTES = (kKBuf + kVBuf) * TILE + 8 * OST;
   static_assert(D == 64, "the LDS layout below is written for d = 64");
   static_assert(IPW * 1024 * (kThreads / 64) == TILE, "tile copies split evenly over the waves");
 };
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   constexpr int BC = C::BC;
   constexpr int ROWB = C::ROWB;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
-  lds_char* const lds = (lds_char*)smem;  // kKBuf K tiles, then kVBuf V tiles
+  lds_char* const lds = (lds_char*)smem;  // kKBuf K tiles, kVBuf V tiles, then 2 KB of O staging per wave
   constexpr int VREG = kKBuf * C::TILE;   // byte offset of the V tiles
 
   const int tid = threadIdx.x;
@@ -505,19 +508,40 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   auto epilogue = [&](const Item& it) {
     const int qi = q0_of(it) + wave * 32 + col;
     const float l_tot = sum_across_halves(l_part);
-    if (qi < Nq_of(it)) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      bf16* orow = O + qbase_of(it) + (size_t)qi * rs;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (half == 0 && qi < Nq_of(it))
+      LSE[lse_base_of(it) + qi] = l_tot > 0.f ? (m_ref + log2_hw(l_tot)) * kLn2 : kNegInf;
+    // O leaves through this wave's 2 KB of LDS, 16 rows at a time: rows
+    // written with their 16-byte chunks at slots c ^ (row % 8), read back
+    // as whole rows and stored with 16-byte non-temporal writes (8 rows per
+    // instruction; O is not read again, so its lines need not stay in L2).
+    // Same wave: program order orders the reads after the writes, and the
+    // second half's writes after the first half's reads.
+    lds_char* const ost = lds + (kKBuf + kVBuf) * C::TILE + wave * C::OST;
+    const int row0 = q0_of(it) + wave * 32;
+    bf16* const obase = O + qbase_of(it);
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
+    for (int h2 = 0; h2 < 2; ++h2) {
+      if ((col >> 4) == h2) {
+        const int rr = col & 15;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                           pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * half) = w;
-        }
-      if (half == 0)
-        LSE[lse_base_of(it) + qi] = l_tot > 0.f ? (m_ref + log2_hw(l_tot)) * kLn2 : kNegInf;
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                             pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+            const int chunk = 4 * db + g;  // dims 8 chunk .. +7; this lane half holds +4 half .. +3
+            *reinterpret_cast<lds_u32x2*>(ost + rr * 128 + ((chunk ^ (rr & 7)) * 16) + 8 * half) = w;
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ci = 64 * i + lane;
+        const int rr = ci >> 3, cc = ci & 7;
+        const u32x4 w = *reinterpret_cast<const lds_u32x4*>(ost + rr * 128 + ((cc ^ (rr & 7)) * 16));
+        const int row = row0 + 16 * h2 + rr;
+        if (row < Nq_of(it)) __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(obase + (size_t)row * rs + cc * 8));
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::NDB; ++i) oacc[i] = f32x16{};
