@@ -65,7 +65,47 @@ def parse():
                    help="seconds of host time for the oracle baseline sample")
     p.add_argument("--sweep-seqlen", action="store_true",
                    help="time prefill and backward against sequence length instead")
+    p.add_argument("--probe-issue", action="store_true",
+                   help="print what one SIMD overlaps (products, vector work, LDS reads) instead")
     return p.parse_args()
+
+
+# (role of waves 0-3, role of waves 4-7, operations each): a role alone, then
+# beside another role on the same SIMDs.
+PROBE_CASES = (
+    ("products", "none", 1024, 0), ("fma", "none", 8192, 0), ("exp", "none", 4096, 0),
+    ("lds16", "none", 2048, 0), ("lds_tr8", "none", 2048, 0),
+    ("product_softmax", "none", 1024, 0), ("product_8fma", "none", 1024, 0),
+    ("products", "fma", 1024, 8192), ("products", "exp", 1024, 4096),
+    ("products", "lds16", 1024, 2048), ("products", "lds_tr8", 1024, 2048),
+    ("products", "products", 1024, 1024), ("product_softmax", "product_softmax", 1024, 1024),
+    ("lds16", "lds16", 2048, 2048), ("lds_tr8", "lds_tr8", 2048, 2048),
+)
+
+
+def probe_issue(fa):
+    """Shader-clock cycles per operation of each wave group (mean over all
+    workgroups, second of two runs), one 8-wave workgroup per CU."""
+    rows = []
+    for ra, rb, na, nb in PROBE_CASES:
+        for _ in range(2):
+            out = fa.fa_probe_issue(ra, rb, na, nb)
+        cyc = out[:, :, 0].double()
+        simd = (out[:, :, 1] >> 4) & 3  # HW_ID bits 5:4
+        simd_ok = bool(simd[:, :4].eq(simd[:, 4:]).all()) and all(
+            len(set(row)) == 4 for row in simd[:, :4].tolist())
+        a = float(cyc[:, :4].mean())
+        b = float(cyc[:, 4:].mean())
+        rows.append((ra, rb, na, nb, a, b, simd_ok))
+        line = f"A={ra:<16} x{na:<5} B={rb:<16} x{nb:<5}  A {a:9.0f} cyc ({a / na:6.2f}/op)"
+        if nb:
+            line += f"  B {b:9.0f} cyc ({b / nb:6.2f}/op)"
+        line += f"  waves w, w+4 share a SIMD: {simd_ok}"
+        print(line, flush=True)
+    simd = ((out[0, :, 1] >> 4) & 3).tolist()
+    print(f"SIMD of waves 0-7 in workgroup 0 (HW_ID bits 5:4): {simd}; HW_ID: "
+          + " ".join(f"{int(x):#010x}" for x in out[0, :, 1]), flush=True)
+    return rows
 
 
 SWEEP_TOKENS = 32768
@@ -296,6 +336,9 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     if args.sweep_seqlen:
         sweep_seqlen(fa, W, dev)
+        return
+    if args.probe_issue:
+        probe_issue(fa)
         return
 
     P = W.LONG_PREFILL

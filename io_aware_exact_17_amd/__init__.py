@@ -58,6 +58,7 @@ SIGNATURES = {
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P,
                              _Z, _P]),
     "fa_probe_read": (_I, [_P, _Z, _P, _P]),
+    "fa_probe_issue": (_I, [_I, _I, _I, _I, _I, _P, _P]),
     "fa_decode_varlen_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
 }
 
@@ -476,6 +477,29 @@ def fa_decode_paged(q, kpages, vpages, block_table, seqlens, max_seqlen, scale=N
                                  int(split_keys), pw, workspace.numel(), _stream(q, stream))
     _check(st, "fa_decode_paged")
     return out, lse
+
+
+PROBE_ROLES = {"none": 0, "products": 1, "fma": 2, "exp": 3, "lds16": 4, "lds_tr8": 5,
+               "product_softmax": 6, "product_8fma": 7}
+
+
+def fa_probe_issue(role_a, role_b, n_a, n_b, grid=None, device=None, stream=None):
+    """Measurement aid (include/fa_probe.h): waves 0-3 of each 8-wave
+    workgroup run `role_a` n_a times, waves 4-7 `role_b` n_b times (roles by
+    name, PROBE_ROLES).  Returns a host int64 tensor [grid, 8, 2]: per wave,
+    shader-clock cycles and the HW_ID register.  `grid` defaults to the
+    device's CU count (one workgroup per CU)."""
+    import torch
+
+    dev = torch.device("cuda" if device is None else device)
+    if grid is None:
+        grid = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.zeros(int(grid), 8, 2, dtype=torch.int64, device=dev)
+    with _on_device(out):
+        st = load().fa_probe_issue(PROBE_ROLES[role_a], PROBE_ROLES[role_b], int(n_a), int(n_b), int(grid),
+                                   ctypes.c_void_p(out.data_ptr()), _stream(out, stream))
+    _check(st, "fa_probe_issue")
+    return out.cpu()
 
 
 def fa_probe_read(buf, nbytes=None, sink=None, stream=None):

@@ -242,6 +242,19 @@ def test_probe_rejects_invalid_arguments():
     assert lib.fa_probe_read(A + 8, 1024, A2, None) == INVALID
 
 
+def test_probe_issue_rejects_invalid_arguments():
+    lib = fa.load()
+    P = fa.PROBE_ROLES
+    ok = (P["products"], P["fma"], 64, 64, 4, A, None)
+    for i, badv in ((0, -1), (0, 8), (1, 8), (2, 12), (3, -8), (2, 1 << 21), (2, 0), (4, 0), (4, 65536),
+                    (5, None), (5, A + 4)):
+        args = list(ok)
+        args[i] = badv
+        assert lib.fa_probe_issue(*args) == INVALID, (i, badv)
+    # a role of none takes no operations
+    assert lib.fa_probe_issue(P["none"], P["none"], 0, 0, 0, A, None) == INVALID  # grid 0
+
+
 def paged_call(q=A, kp=A, vp=A, bt=A2, sl=A2, o=A2, lse=A2, B=2, H=4, d=128, page=16,
                num_pages=100, max_blocks=8, max_seqlen=100, scale=0.1, split_keys=0,
                ws=A, ws_bytes=1 << 30):

@@ -626,3 +626,20 @@ def test_probe_read_runs(fa):
     fa.fa_probe_read(buf, nbytes=4096 + 16, sink=sink)  # a ragged last workgroup
     torch.cuda.synchronize()
     assert sink.item() == 7
+
+
+def test_probe_issue_runs(fa):
+    """The issue probe (a measurement aid) times every role on a few
+    workgroups: positive cycle counts, and a product alone costs at least its
+    32 pipeline cycles (8 passes of 4) and not absurdly more."""
+    log("case probe issue")
+    for ra, rb, na, nb in (("products", "none", 64, 0), ("lds_tr8", "lds16", 64, 64),
+                           ("product_softmax", "product_8fma", 64, 64), ("fma", "exp", 64, 64)):
+        out = fa.fa_probe_issue(ra, rb, na, nb, grid=4)
+        cyc = out[:, :, 0]
+        assert bool((cyc[:, :4] > 0).all()), (ra, rb)
+        if nb:
+            assert bool((cyc[:, 4:] > 0).all()), (ra, rb)
+    out = fa.fa_probe_issue("products", "none", 1024, 0, grid=4)
+    per_op = float(out[:, :4, 0].double().mean()) / 1024
+    assert 28.0 <= per_op <= 200.0, per_op
