@@ -88,6 +88,23 @@ def test_prefill_full_size_sampled(fa, spec):
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefill_very_long_sampled(fa, d):
+    """A sequence eight times the long prefill's (N = 65536, causal, two
+    heads): 256 query tiles per head and walks of up to 1024 key tiles, in
+    the streaming launch; sampled rows against the oracle."""
+    B, H, N = 1, 2, 65536
+    log(f"case very long prefill N={N} d={d}")
+    q, k, v = W.prefill_inputs(B, H, N, N, d, "bf16", seed=4242 + d, device="cuda")
+    scale = d ** -0.5
+    o, lse = run_fwd(fa, q, k, v, scale, True)
+    rows = _sampled_rows(B, H, N, 1, 24, 4242 + d) + [(0, 1, N - 2), (0, 0, N // 2)]
+    O, L = oracle.attention_rows(q, k, v, scale, True, rows)
+    idx = tuple(torch.as_tensor(a, device=o.device) for a in np.array(rows).T)
+    check(o[idx].cpu(), lse[idx].cpu(), O, L, TOL_BF16, f"N={N} d={d}")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
 def test_long_prefill_whole_output(fa):
     """The long causal prefill (B=1, H=32, N=8192, d=128) in the launch the
     benchmark times: every element of O and LSE of all 32 heads against the
