@@ -303,6 +303,22 @@ def test_decode_edge_lengths(fa, d):
         assert (o[1] == 0).all() and torch.isneginf(lse[1]).all()
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_very_long(fa, d):
+    """Decode over 262144 cached tokens (with a shorter sequence beside it):
+    256 chunks of 1024 keys for one (sequence, head), merged across XCDs,
+    and the merge kernel path for a finer split; every output against the
+    oracle."""
+    lens = [262144, 100003]
+    log(f"case decode very long d={d}")
+    q, kc, vc, sl, off = W.decode_inputs(len(lens), 4, d, lens, seed=23 + d, device="cuda")
+    scale = 1 / math.sqrt(d)
+    O, L = oracle.decode(q, kc, vc, sl.cpu(), off.cpu(), scale)
+    for sk in (0, 256):
+        o, lse = run_decode(fa, q, kc, vc, sl, off, max(lens), scale, sk)
+        check(o, lse, O, L, TOL_BF16, f"d={d} split_keys={sk}")
+
+
 def test_decode_split_invariance(fa):
     s = W.DECODE_SINGLE
     log("case decode split invariance")
