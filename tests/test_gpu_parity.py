@@ -412,11 +412,18 @@ VARLEN_CASES = [
     (64, False, [200, 40], [77, 3000]),
     (64, True, [300, 0, 70, 5], [64, 5, 0, 700]),     # empty sequence, keyless rows
 ]
+# Many short sequences of seeded random lengths (empty ones among them): a
+# grid of hundreds of sequences, most a single query tile.
+_MANY = [int(x) for x in np.random.default_rng(5).integers(0, 300, 400)]
+VARLEN_CASES += [
+    (128, True, _MANY, _MANY),
+    (64, False, _MANY, _MANY[::-1]),
+]
 
 
 @pytest.mark.parametrize("d,causal,lq,lk", VARLEN_CASES)
 def test_fwd_varlen(fa, d, causal, lq, lk):
-    log(f"case varlen d={d} causal={causal} lq={lq} lk={lk}")
+    log(f"case varlen d={d} causal={causal} lq={lq[:8]} ({len(lq)} sequences) lk={lk[:8]}")
     H = 3
     q, k, v, cq, ck = W.varlen_inputs(lq, lk, H, d, seed=61 + d + len(lq), device="cuda")
     o, lse = fa.fa_fwd_varlen(q, k, v, cq, ck, max(lq), 1 / math.sqrt(d), causal)
