@@ -80,6 +80,8 @@ PROBE_CASES = (
     ("products", "lds16", 1024, 2048), ("products", "lds_tr8", 1024, 2048),
     ("products", "products", 1024, 1024), ("product_softmax", "product_softmax", 1024, 1024),
     ("lds16", "lds16", 2048, 2048), ("lds_tr8", "lds_tr8", 2048, 2048),
+    ("products", "product_softmax", 1024, 1024), ("products", "product_8fma", 1024, 1024),
+    ("products", "product_8fma", 2048, 1024),
 )
 
 
