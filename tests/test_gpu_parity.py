@@ -537,6 +537,24 @@ def test_bwd(fa, d, causal, B, H, Nq, Nk):
     check_grads(grads, oracle.attention_grad(q, k, v, do, sc, causal), "bwd")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_bwd_deterministic(fa, d):
+    """The backward is run-to-run bit-identical: no atomics, every gradient
+    element accumulated in a fixed order by one wave."""
+    log(f"case bwd determinism d={d}")
+    B, H, N = 2, 3, 777
+    q, k, v = W.prefill_inputs(B, H, N, N, d, "bf16", seed=31 + d, device="cuda")
+    do = W.prefill_inputs(B, H, N, 1, d, "bf16", seed=32 + d, device="cuda")[0]
+    sc = 1 / math.sqrt(d)
+    for causal in (True, False):
+        o, lse = fa.fa_fwd(q, k, v, sc, causal)
+        g1 = fa.fa_bwd(q, k, v, o, do, lse, sc, causal)
+        g2 = fa.fa_bwd(q, k, v, o, do, lse, sc, causal)
+        torch.cuda.synchronize()
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b), causal
+
+
 def test_bwd_full_size_one_head(fa):
     """The long causal shape (B=1, H=32, N=8192, d=128) through forward and
     backward on the GPU; one whole head's three gradients against the oracle."""
